@@ -1,0 +1,269 @@
+"""Benchmark of the block-scaled int8 projection on one MI355X.
+
+One step is one pass of the whole prefill path over one batch of the prefill
+attention-projection workload (M=2048, N=4096, K=4096): the NVFP4 -> int8
+weight requant, the BF16 -> int8 activation requant and the block-scaled int8
+GEMM, all through the C ABI.  `value` is 2*M*N*K / step time (TOPS).  The
+decode GEMV (M in {1,2,4,8}) is timed in the same run on its own workload and
+reported under "decode" in GB/s of algorithmic HBM traffic.
+
+Inputs are resident in HBM before timing.  Every timed iteration uses a
+different set of buffers (rotating through enough sets that each set has left
+the 256 MB Infinity Cache before it is used again).  Per-kernel durations come
+from HIP events recorded around each launch on the stream the launches use.
+The CPU oracle is timed beside it on a bounded sample (rank 0, one GPU only).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "int8 block-scaled GEMM TOPS (prefill) + GEMV HBM GB/s, % of MI355X peak"
+PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--decode-iters", type=int, default=100)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
+    p.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    return p.parse_args()
+
+
+def _source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "block_scaled_precision_requant_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel, source_files, launches_bytes_alg):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when the summary is missing or the kernel source changed since it was taken."""
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != _source_digest(source_files):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = _args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              f"the multi-GPU sharding is a design note, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import oracle
+    from block_scaled_precision_requant_amd import bsr, inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    rec = {}
+
+    def dev_t(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    # ------------------------------------------------------------ prefill
+    proj = inputs.workload("attn_proj").projections[0]
+    M, N, K = proj.m, proj.n, proj.k
+    packed, e4m3 = proj.weight()
+    a_bits = proj.activations()
+    set_bytes = (N * K // 2 + N * K // 16 + N * K + N * K // 8 + 2 * M * K + M * K + M * K // 8 + 2 * M * N)
+    nsets = max(2, int(np.ceil(1.0 * 2 ** 30 / set_bytes)))
+    sets = []
+    for _ in range(nsets):
+        sets.append(dict(
+            wp=dev_t(packed), we=dev_t(e4m3), a=dev_t(a_bits.view(np.int16)),
+            w_i8=torch.empty((N, K), dtype=torch.int8, device=dev),
+            w_s=torch.empty((N, K // 32), dtype=torch.float32, device=dev),
+            a_i8=torch.empty((M, K), dtype=torch.int8, device=dev),
+            a_s=torch.empty((M, K // 32), dtype=torch.float32, device=dev),
+            out=torch.empty((M, N), dtype=torch.int16, device=dev)))
+    scale2 = float(proj.scale2)
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        bsr.requant_w_nvfp4_int8(s["wp"], s["we"], scale2, s["w_i8"], s["w_s"], stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        bsr.requant_a_int8(s["a"], s["a_i8"], s["a_s"], stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        bsr.int8_gemm_blockscaled(s["a_i8"], s["w_i8"], s["a_s"], s["w_s"], s["out"], stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    if args.only in ("all", "prefill"):
+        for i in range(args.warmup):
+            step(sets[i % nsets])
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(sets[i % nsets], evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        t_w = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+        t_a = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+        t_g = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e-3
+        ms_per_step = wall / args.steps * 1e3
+        ops = 2.0 * M * N * K
+        gemm_tops = ops / t_g.mean() / 1e12
+        bytes_w = N * K * (0.5 + 1 / 16 + 1 + 1 / 8)
+        bytes_a = M * K * (2 + 1 + 1 / 8)
+        rec["prefill"] = dict(
+            ms_per_step=ms_per_step, value_tops=ops / (ms_per_step * 1e-3) / 1e12,
+            kernels={
+                "requant_w_nvfp4_int8": dict(us_mean=t_w.mean() * 1e6, us_min=t_w.min() * 1e6,
+                                             gbs=bytes_w / t_w.mean() / 1e9,
+                                             frac_hbm=bytes_w / t_w.mean() / 1e9 / PEAK_HBM_GBS),
+                "requant_a_int8": dict(us_mean=t_a.mean() * 1e6, us_min=t_a.min() * 1e6,
+                                       gbs=bytes_a / t_a.mean() / 1e9,
+                                       frac_hbm=bytes_a / t_a.mean() / 1e9 / PEAK_HBM_GBS),
+                "int8_gemm_blockscaled": dict(us_mean=t_g.mean() * 1e6, us_min=t_g.min() * 1e6,
+                                              tops=gemm_tops, frac_int8=gemm_tops / PEAK_INT8_TOPS),
+            },
+            buffer_sets=nsets)
+        # parity of the timed outputs (last set used), sampled rows against the oracle
+        s = sets[(args.steps - 1) % nsets]
+        rows = np.array([0, 1, 777, M - 1])
+        ow, osw = oracle.requant_w(packed, e4m3, proj.scale2)
+        oa, osa = oracle.requant_a(a_bits[rows])
+        y, t = oracle.gemm_ref(oa, ow, osa, osw)
+        from oracle.compare import check_bf16
+        res = check_bf16(s["out"][torch.as_tensor(rows, device=dev)].cpu().numpy().view(np.uint16), y, t, K)
+        rec["prefill"]["parity_sampled_rows"] = dict(rows=len(rows), ok=res.ok, failures=res.failures)
+
+    # ------------------------------------------------------------ decode
+    if args.only in ("all", "decode"):
+        dec = {}
+        for p in inputs.workload("decode").projections:
+            wp, we = p.weight()
+            a = p.activations()
+            w_i8 = torch.empty((p.n, p.k), dtype=torch.int8, device=dev)
+            w_s = torch.empty((p.n, p.k // 32), dtype=torch.float32, device=dev)
+            bsr.requant_w_nvfp4_int8(dev_t(wp), dev_t(we), float(p.scale2), w_i8, w_s)
+            wbytes = p.n * p.k * 1.125
+            ncopy = max(2, int(np.ceil(2 ** 30 / wbytes)))
+            copies = [(w_i8.clone(), w_s.clone()) for _ in range(ncopy)]
+            a_dev = dev_t(a.view(np.int16))
+            a_i8 = torch.empty((p.m, p.k), dtype=torch.int8, device=dev)
+            a_s = torch.empty((p.m, p.k // 32), dtype=torch.float32, device=dev)
+            out = torch.empty((p.m, p.n), dtype=torch.int16, device=dev)
+            bsr.requant_a_int8(a_dev, a_i8, a_s)
+            for i in range(10):
+                wi, ws = copies[i % ncopy]
+                bsr.int8_gemm_blockscaled(a_i8, wi, a_s, ws, out)
+            torch.cuda.synchronize()
+            it = args.decode_iters
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(it)]
+            for i in range(it):
+                wi, ws = copies[i % ncopy]
+                evs[i][0].record(stream)
+                bsr.requant_a_int8(a_dev, a_i8, a_s, stream=stream)
+                evs[i][1].record(stream)
+                bsr.int8_gemm_blockscaled(a_i8, wi, a_s, ws, out, stream=stream)
+                evs[i][2].record(stream)
+            torch.cuda.synchronize()
+            t_q = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+            t_v = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+            alg = p.n * p.k * 1.125 + p.m * p.k * 1.125 + 2 * p.m * p.n
+            dec[p.name] = dict(m=p.m, n=p.n, k=p.k, gemv_us_mean=t_v.mean() * 1e6,
+                               gemv_us_median=float(np.median(t_v)) * 1e6, gemv_us_min=t_v.min() * 1e6,
+                               gemv_gbs=alg / t_v.mean() / 1e9,
+                               gemv_frac_hbm=alg / t_v.mean() / 1e9 / PEAK_HBM_GBS,
+                               requant_a_plus_gemv_us=(t_q + t_v).mean() * 1e6)
+            del copies
+            torch.cuda.empty_cache()
+        gbs = [d["gemv_gbs"] for d in dec.values()]
+        rec["decode"] = dict(cases=dec, gemv_gbs_mean=float(np.mean(gbs)),
+                             gemv_frac_hbm_mean=float(np.mean(gbs)) / PEAK_HBM_GBS)
+
+    # ------------------------------------------------------------ CPU oracle
+    cpu = None
+    if not args.no_cpu_baseline and args.only in ("all", "prefill"):
+        cores = oracle.max_threads()
+        t0 = time.perf_counter()
+        ow, osw = oracle.requant_w(packed, e4m3, proj.scale2)
+        t_rw = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oa, osa = oracle.requant_a(a_bits)
+        t_ra = time.perf_counter() - t0
+        rows_done, t_rows = 0, 0.0
+        budget = max(1.0, args.cpu_seconds - t_rw - t_ra)
+        chunk = max(1, cores)
+        while t_rows < budget and rows_done < M:
+            r = np.arange(rows_done, min(M, rows_done + chunk))
+            t0 = time.perf_counter()
+            oracle.gemm_ref(oa[r], ow, osa[r], osw)
+            t_rows += time.perf_counter() - t0
+            rows_done += len(r)
+        t_full = t_rw + t_ra + t_rows * M / rows_done
+        cpu = dict(value=2.0 * M * N * K / t_full / 1e12, unit="TOPS", cores=cores, kind="oracle",
+                   sample=(f"full weight and activation requant ({t_rw:.2f} s + {t_ra:.2f} s), "
+                           f"GEMM reference on {rows_done} of {M} rows ({t_rows:.2f} s) "
+                           f"extrapolated linearly to all rows"),
+                   seconds_extrapolated=t_full)
+
+    pre = rec.get("prefill")
+    line = {
+        "metric": METRIC,
+        "value": pre["value_tops"] if pre else None,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["ms_per_step"] if pre else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"prefill attention projection M={M} N={N} K={K} "
+                               "(A ~ N(0,1) BF16, NVFP4 W scales 2^U{-4..2}, scale2 = fl32(1/448))",
+                   "m": M, "n": N, "k": K,
+                   "step": "requant_w_nvfp4_int8 + requant_a_int8 + int8_gemm_blockscaled"},
+    }
+    if pre:
+        g = pre["kernels"]["int8_gemm_blockscaled"]
+        line["roofline"] = {"bound": "mfma", "achieved": g["tops"], "peak": PEAK_INT8_TOPS,
+                            "unit": "TOPS", "frac": g["tops"] / PEAK_INT8_TOPS,
+                            "traffic": _traffic("gemm_kernel", ["gemm.hip", "bsr_internal.h"], None),
+                            "kernel": "gemm_kernel (int8_gemm_blockscaled, m > 8)"}
+        line["kernels"] = pre["kernels"]
+        line["parity"] = pre["parity_sampled_rows"]
+    if cpu:
+        line["cpu_baseline"] = cpu
+    if "decode" in rec:
+        line["decode"] = rec["decode"]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,138 @@
+"""Python binding of libbsr: the C-ABI entry points under the same names.
+
+Argument marshalling only -- every step runs in the HIP kernels of libbsr.so.
+Tensors must be CUDA (HIP) tensors; their data pointers, sizes derived from
+their shapes, and a stream (default: torch's current stream on the tensors'
+device) are passed straight through.  A non-zero status raises ``BsrError``.
+There is no fallback: if libbsr.so is missing, the first call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsr.so")
+
+BSR_OK, BSR_EINVAL, BSR_ENULL, BSR_EALIGN, BSR_EDEVICE, BSR_ELAUNCH = range(6)
+PATH_AUTO, PATH_GEMM, PATH_GEMV = 0, 1, 2
+GEMV_MAX_ROWS = 8
+
+# Exported symbols and their C signatures (kept in step with include/bsr.h).
+_vp, _u32, _f32, _int = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_float, ctypes.c_int
+SIGNATURES = {
+    "requant_w_nvfp4_int8": (_int, [_vp, _vp, _f32, _vp, _vp, _u32, _u32, _vp]),
+    "requant_a_int8": (_int, [_vp, _vp, _vp, _u32, _u32, _vp]),
+    "int8_gemm_blockscaled": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u32, _u32, _vp]),
+    "int8_gemm_blockscaled_ex": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u32, _u32, _vp, _int]),
+    "bsr_status_string": (ctypes.c_char_p, [_int]),
+}
+
+_LIB = None
+
+
+class BsrError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+def lib():
+    """The loaded libbsr.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; "
+                               f"g.build()'` or `python block_scaled_precision_requant_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return lib().bsr_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream, like):
+    if stream is None:
+        stream = torch.cuda.current_stream(like.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _shape(t, shape, what):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{what}: must be a device tensor")
+
+
+def _done(status, what):
+    if status != BSR_OK:
+        raise BsrError(status, what)
+
+
+def requant_w_nvfp4_int8(w_packed, w_e4m3, scale2, w_i8, w_scale, stream=None):
+    """NVFP4 weight (w_packed [N,K/2] u8, w_e4m3 [N,K/16] u8, scale2 float) ->
+    w_i8 [N,K] int8 and w_scale [N,K/32] float32 (both preallocated)."""
+    n, half_k = w_packed.shape
+    k = 2 * half_k
+    _shape(w_packed, (n, k // 2), "w_packed")
+    _shape(w_e4m3, (n, k // 16), "w_e4m3")
+    _shape(w_i8, (n, k), "w_i8")
+    _shape(w_scale, (n, k // 32), "w_scale")
+    st = lib().requant_w_nvfp4_int8(_ptr(w_packed), _ptr(w_e4m3), float(scale2), _ptr(w_i8),
+                                    _ptr(w_scale), n, k, _stream(stream, w_i8))
+    _done(st, "requant_w_nvfp4_int8")
+
+
+def requant_a_int8(a_bf16, a_i8, a_scale, stream=None):
+    """BF16 activations a_bf16 [M,K] -> a_i8 [M,K] int8 and a_scale [M,K/32] float32."""
+    m, k = a_bf16.shape
+    _shape(a_bf16, (m, k), "a_bf16")
+    _shape(a_i8, (m, k), "a_i8")
+    _shape(a_scale, (m, k // 32), "a_scale")
+    st = lib().requant_a_int8(_ptr(a_bf16), _ptr(a_i8), _ptr(a_scale), m, k, _stream(stream, a_i8))
+    _done(st, "requant_a_int8")
+
+
+def int8_gemm_blockscaled_ex(a_i8, w_i8, a_scale, w_scale, out, path=PATH_AUTO, stream=None):
+    """out [M,N] BF16 = block-scaled int8 GEMM of a_i8 [M,K] and w_i8 [N,K]."""
+    m, k = a_i8.shape
+    n = w_i8.shape[0]
+    _shape(a_i8, (m, k), "a_i8")
+    _shape(w_i8, (n, k), "w_i8")
+    _shape(a_scale, (m, k // 32), "a_scale")
+    _shape(w_scale, (n, k // 32), "w_scale")
+    _shape(out, (m, n), "out")
+    st = lib().int8_gemm_blockscaled_ex(_ptr(a_i8), _ptr(w_i8), _ptr(a_scale), _ptr(w_scale), _ptr(out),
+                                        m, n, k, _stream(stream, out), int(path))
+    _done(st, "int8_gemm_blockscaled_ex")
+
+
+def int8_gemm_blockscaled(a_i8, w_i8, a_scale, w_scale, out, stream=None):
+    """As int8_gemm_blockscaled_ex with the automatic path (GEMV iff M <= 8)."""
+    m, k = a_i8.shape
+    n = w_i8.shape[0]
+    _shape(a_i8, (m, k), "a_i8")
+    _shape(w_i8, (n, k), "w_i8")
+    _shape(a_scale, (m, k // 32), "a_scale")
+    _shape(w_scale, (n, k // 32), "w_scale")
+    _shape(out, (m, n), "out")
+    st = lib().int8_gemm_blockscaled(_ptr(a_i8), _ptr(w_i8), _ptr(a_scale), _ptr(w_scale), _ptr(out),
+                                     m, n, k, _stream(stream, out))
+    _done(st, "int8_gemm_blockscaled")
+
+
+def prefill(a_bf16, w_i8, w_scale, a_i8_scratch, a_scale_scratch, out, stream=None):
+    """The two-launch projection: requant_a_int8 then int8_gemm_blockscaled on one stream."""
+    requant_a_int8(a_bf16, a_i8_scratch, a_scale_scratch, stream=stream)
+    int8_gemm_blockscaled(a_i8_scratch, w_i8, a_scale_scratch, w_scale, out, stream=stream)

@@ -1,0 +1,115 @@
+// api.hip -- the C ABI of libbsr: argument validation, the m <= 8 dispatch
+// and the launches.  Every check happens before the first launch; an error
+// launches nothing.  The only state is a per-device cache of the gfx950 check.
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "bsr.h"
+#include "bsr_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return BSR_EDEVICE;
+    if (dev >= kMaxDevices) return BSR_EDEVICE;
+    int state = g_device_ok[dev].load(std::memory_order_relaxed);
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BSR_EDEVICE;
+        state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_device_ok[dev].store(state, std::memory_order_relaxed);
+    }
+    return state == 1 ? BSR_OK : BSR_EDEVICE;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool k_ok(uint32_t k) { return k != 0 && k % 32 == 0; }
+
+// Grids stay below 2^31 workgroups.
+constexpr uint64_t kMaxGrid = (1ull << 31) - 1;
+
+int launched(hipError_t e) { return e == hipSuccess ? BSR_OK : BSR_ELAUNCH; }
+
+int gemm_args_check(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
+                    const float *w_scale, const uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                    int path) {
+    if (!k_ok(k)) return BSR_EINVAL;
+    if (path != BSR_PATH_AUTO && path != BSR_PATH_GEMM && path != BSR_PATH_GEMV) return BSR_EINVAL;
+    if (m == 0 || n == 0) return BSR_OK;
+    if (path == BSR_PATH_GEMV && m > (uint32_t)bsr::kGemvMaxRows) return BSR_EINVAL;
+    if (!a_i8 || !w_i8 || !a_scale || !w_scale || !out) return BSR_ENULL;
+    if (!aligned(a_i8, 16) || !aligned(w_i8, 16) || !aligned(a_scale, 4) || !aligned(w_scale, 4) ||
+        !aligned(out, 2))
+        return BSR_EALIGN;
+    const uint64_t tiles = bsr::div_up(m, bsr::kGemmBM) * bsr::div_up(n, bsr::kGemmBN);
+    if (tiles > kMaxGrid) return BSR_EINVAL;
+    return BSR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int requant_w_nvfp4_int8(const uint8_t *w_packed, const uint8_t *w_e4m3, float scale2,
+                         int8_t *w_i8, float *w_scale, uint32_t n, uint32_t k, void *stream) {
+    if (!k_ok(k) || !std::isfinite(scale2)) return BSR_EINVAL;
+    if (n == 0) return BSR_OK;
+    if (!w_packed || !w_e4m3 || !w_i8 || !w_scale) return BSR_ENULL;
+    if (!aligned(w_packed, 16) || !aligned(w_e4m3, 2) || !aligned(w_i8, 16) || !aligned(w_scale, 4))
+        return BSR_EALIGN;
+    const uint64_t nblocks = (uint64_t)n * (k / 32);
+    if (bsr::div_up(nblocks, bsr::kRqwThreads) > kMaxGrid) return BSR_EINVAL;
+    if (int st = check_device()) return st;
+    return launched(bsr::launch_requant_w(w_packed, w_e4m3, scale2, w_i8, w_scale, nblocks,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int requant_a_int8(const uint16_t *a_bf16, int8_t *a_i8, float *a_scale, uint32_t m, uint32_t k,
+                   void *stream) {
+    if (!k_ok(k)) return BSR_EINVAL;
+    if (m == 0) return BSR_OK;
+    if (!a_bf16 || !a_i8 || !a_scale) return BSR_ENULL;
+    if (!aligned(a_bf16, 16) || !aligned(a_i8, 16) || !aligned(a_scale, 4)) return BSR_EALIGN;
+    const uint64_t nblocks = (uint64_t)m * (k / 32);
+    if (bsr::div_up(nblocks * bsr::kRqaLanesPerBlock, bsr::kRqaThreads) > kMaxGrid) return BSR_EINVAL;
+    if (int st = check_device()) return st;
+    return launched(bsr::launch_requant_a(a_bf16, a_i8, a_scale, nblocks, static_cast<hipStream_t>(stream)));
+}
+
+int int8_gemm_blockscaled_ex(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
+                             const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                             void *stream, int path) {
+    if (int st = gemm_args_check(a_i8, w_i8, a_scale, w_scale, out, m, n, k, path)) return st;
+    if (m == 0 || n == 0) return BSR_OK;
+    if (int st = check_device()) return st;
+    const bool gemv = path == BSR_PATH_GEMV || (path == BSR_PATH_AUTO && m <= (uint32_t)bsr::kGemvMaxRows);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (gemv) return launched(bsr::launch_gemv(a_i8, w_i8, a_scale, w_scale, out, m, n, k, s));
+    return launched(bsr::launch_gemm(a_i8, w_i8, a_scale, w_scale, out, m, n, k, s));
+}
+
+int int8_gemm_blockscaled(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
+                          const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                          void *stream) {
+    return int8_gemm_blockscaled_ex(a_i8, w_i8, a_scale, w_scale, out, m, n, k, stream, BSR_PATH_AUTO);
+}
+
+const char *bsr_status_string(int status) {
+    switch (status) {
+    case BSR_OK: return "BSR_OK";
+    case BSR_EINVAL: return "BSR_EINVAL: invalid size or argument";
+    case BSR_ENULL: return "BSR_ENULL: null pointer";
+    case BSR_EALIGN: return "BSR_EALIGN: misaligned pointer";
+    case BSR_EDEVICE: return "BSR_EDEVICE: no current gfx950 device";
+    case BSR_ELAUNCH: return "BSR_ELAUNCH: kernel launch failed";
+    default: return "unknown bsr status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// bsr_internal.h -- launch geometry and device helpers shared by the kernels
+// and the C-ABI layer.  Every geometry constant lives here once: the kernels
+// are compiled against these values and the host derives grids from them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsr {
+
+// ---- requant kernels ------------------------------------------------------
+// Activation requant: one lane per 16-byte chunk (8 BF16), four lanes per
+// 32-element block, 256 lanes per workgroup.
+constexpr int kRqaThreads = 256;
+constexpr int kRqaLanesPerBlock = 4;
+// Weight requant: one lane per 32-element block (16 packed bytes in,
+// 32 int8 out), 256 lanes per workgroup.
+constexpr int kRqwThreads = 256;
+
+// ---- GEMM (m > 8) ---------------------------------------------------------
+// A workgroup of 4 waves computes a kGemmBM x kGemmBN output tile; each wave
+// owns a 64 x 64 quarter as 2 x 2 MFMA 32x32x32 int8 tiles.  The K loop
+// stages kGemmStageBlocks 32-wide blocks of A and W per LDS pass.
+constexpr int kGemmThreads = 256;
+constexpr int kGemmBM = 128;
+constexpr int kGemmBN = 128;
+constexpr int kGemmStageBlocks = 4;
+constexpr int kGemmStageBytes = 32 * kGemmStageBlocks;   // 128 bytes of K per row
+constexpr int kGemmLdsRowStride = kGemmStageBytes + 16;   // pad: rows start 4 banks apart
+
+// ---- GEMV (m <= 8) --------------------------------------------------------
+// kGemvLanesPerCol lanes split the K blocks of one output column; a wave
+// covers 64 / kGemvLanesPerCol columns, a workgroup kGemvThreads / kGemvLanesPerCol.
+constexpr int kGemvThreads = 256;
+constexpr int kGemvLanesPerCol = 16;
+constexpr int kGemvColsPerWg = kGemvThreads / kGemvLanesPerCol;
+constexpr int kGemvMaxRows = 8;
+
+inline uint64_t div_up(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+// Launchers (no validation: the C-ABI layer has checked every argument).
+hipError_t launch_requant_w(const uint8_t *w_packed, const uint8_t *w_e4m3, float scale2,
+                            int8_t *w_i8, float *w_scale, uint64_t nblocks, hipStream_t s);
+hipError_t launch_requant_a(const uint16_t *a_bf16, int8_t *a_i8, float *a_scale,
+                            uint64_t nblocks, hipStream_t s);
+hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
+                       const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
+                       uint32_t k, hipStream_t s);
+hipError_t launch_gemv(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
+                       const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
+                       uint32_t k, hipStream_t s);
+
+}  // namespace bsr
+
+namespace bsr {
+// BF16 round-to-nearest-even of a finite or infinite binary32.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+    uint32_t u = __float_as_uint(x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+}  // namespace bsr

@@ -1,0 +1,207 @@
+// requant.hip -- the two per-32 int8 quantizers for gfx950.
+//
+// Both follow page "metrale_model_layers/layers/ops/gemm_dense_int8.rs": the
+// doc comment of `requant_w_nvfp4_int8` (NVFP4 weight -> int8 + F32 per 32)
+// and the first launch of `int8_gemm_faith2_prefill` (BF16 activations ->
+// int8 + F32 per 32).  Per block: amax = max|v|, s = fl32(amax/127),
+// q = clamp(rne(fl32(v/s)), -127, 127); s == 0 gives +0.0f and q = 0.
+// Results are bit-identical to that definition; the code only reorganises
+// how the quotient's rounding is obtained:
+//
+//  * BF16 path: q0 = v * r with r ~ 1/s.  |q0 - v/s| < 2^-15 for |q0| <= 128,
+//    so whenever q0 sits more than 2^-14 away from a half-integer, rne(q0)
+//    equals rne(fl32(v/s)).  Elements closer than that take the IEEE divide.
+//    A power-of-two s has an exact reciprocal (q0 is then exact); a subnormal
+//    s takes the IEEE divide and the clamp for the whole block.
+//  * NVFP4 path: a half-block holds one E4M3 scale, so its 16 elements take at
+//    most 8 magnitudes.  The 7 non-zero magnitudes of each half are divided
+//    (IEEE) once, and every element picks its code with a byte permute.
+#include "bsr_internal.h"
+
+namespace bsr {
+namespace {
+
+constexpr float kTieGuard = 0.5f - 0x1p-14f;
+
+// Max over the four lanes of a quad (the lanes of one 32-element block).
+__device__ __forceinline__ float quad_max(float x) {
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true)));
+    return x;
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+    return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
+           ((uint32_t)d << 24);
+}
+
+__global__ __launch_bounds__(kRqaThreads) void requant_a_kernel(const uint4 *__restrict__ a,
+                                                                uint2 *__restrict__ q,
+                                                                float *__restrict__ scale,
+                                                                uint64_t nchunks) {
+    const uint64_t c = (uint64_t)blockIdx.x * kRqaThreads + threadIdx.x;
+    // nchunks is a multiple of 4 and so is every quad's first lane: a quad is
+    // either wholly live or wholly idle.
+    const bool live = c < nchunks;
+    const uint4 raw = live ? a[c] : make_uint4(0, 0, 0, 0);
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(wd[i] << 16);
+        v[2 * i + 1] = __uint_as_float(wd[i] & 0xFFFF0000u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = quad_max(amax);
+    const float s = amax / 127.0f;
+
+    float t[8];
+    if (s == 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = 0.0f;
+    } else if (s < 0x1p-126f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = fminf(fmaxf(rintf(v[i] / s), -127.0f), 127.0f);
+    } else {
+        const uint32_t sb = __float_as_uint(s);
+        const bool pow2 = (sb & 0x007FFFFFu) == 0;
+        const float r = pow2 ? __uint_as_float(0x7F000000u - (sb & 0x7F800000u))
+                             : __builtin_amdgcn_rcpf(s);
+        uint32_t near = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float q0 = v[i] * r;
+            t[i] = rintf(q0);
+            near |= (fabsf(q0 - t[i]) > kTieGuard) ? (1u << i) : 0u;
+        }
+        if (!pow2 && near) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (near & (1u << i)) t[i] = rintf(v[i] / s);
+        }
+    }
+    if (live) {
+        q[c] = make_uint2(pack4_i8((int)t[0], (int)t[1], (int)t[2], (int)t[3]),
+                          pack4_i8((int)t[4], (int)t[5], (int)t[6], (int)t[7]));
+        if ((c & 3) == 0) scale[c >> 2] = s;
+    }
+}
+
+// OCP E4M3 code -> binary32.  Its exponent and mantissa bits shifted into a
+// binary32 give the value times 2^-120 (E4M3 subnormals land on binary32
+// subnormals), so one exact multiply restores it.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+    const float mag = __uint_as_float((code & 0x7Fu) << 20) * 0x1p120f;
+    return (code & 0x80u) ? -mag : mag;
+}
+
+// E2M1 magnitude code (0..7) -> binary32: the 3 bits shifted into a binary32
+// give the value times 2^-126 (code 1 lands on a subnormal).
+__device__ __forceinline__ float e2m1_mag_to_f32(uint32_t mcode) {
+    return __uint_as_float(mcode << 22) * 0x1p126f;
+}
+
+// Highest magnitude code (0..7) among the 16 nibbles of two packed dwords.
+__device__ __forceinline__ uint32_t max_mag_code(uint32_t w0, uint32_t w1) {
+    // perm with a byte table {1,2,4,...,128} turns each 3-bit code into a one-hot byte.
+    const uint32_t t_lo = 0x08040201u, t_hi = 0x80402010u;
+    uint32_t x = __builtin_amdgcn_perm(t_hi, t_lo, w0 & 0x07070707u) |
+                 __builtin_amdgcn_perm(t_hi, t_lo, (w0 >> 4) & 0x07070707u) |
+                 __builtin_amdgcn_perm(t_hi, t_lo, w1 & 0x07070707u) |
+                 __builtin_amdgcn_perm(t_hi, t_lo, (w1 >> 4) & 0x07070707u);
+    x |= x >> 16;
+    x |= x >> 8;
+    return 31u - (uint32_t)__builtin_clz(x & 0xFFu);  // x != 0: every nibble sets a bit
+}
+
+// 8 codes of one packed dword -> 8 int8 (two dwords), given the byte tables
+// of the half: pos = q of magnitude codes 0..7, neg = their negations.
+__device__ __forceinline__ uint2 lookup8(uint32_t w, uint32_t pos_lo, uint32_t pos_hi,
+                                         uint32_t neg_lo, uint32_t neg_hi) {
+    const uint32_t w4 = w >> 4;
+    const uint32_t sel_e = w & 0x07070707u, sel_o = w4 & 0x07070707u;
+    const uint32_t sg_e = w & 0x08080808u, sg_o = w4 & 0x08080808u;
+    const uint32_t mask_e = (sg_e << 5) - (sg_e >> 3);  // 0xFF in bytes whose sign bit is set
+    const uint32_t mask_o = (sg_o << 5) - (sg_o >> 3);
+    const uint32_t ev = (mask_e & __builtin_amdgcn_perm(neg_hi, neg_lo, sel_e)) |
+                        (~mask_e & __builtin_amdgcn_perm(pos_hi, pos_lo, sel_e));
+    const uint32_t od = (mask_o & __builtin_amdgcn_perm(neg_hi, neg_lo, sel_o)) |
+                        (~mask_o & __builtin_amdgcn_perm(pos_hi, pos_lo, sel_o));
+    // interleave: elements 0..3 = ev.b0 od.b0 ev.b1 od.b1, elements 4..7 = ev.b2 od.b2 ev.b3 od.b3
+    return make_uint2(__builtin_amdgcn_perm(od, ev, 0x05010400u),
+                      __builtin_amdgcn_perm(od, ev, 0x07030602u));
+}
+
+__global__ __launch_bounds__(kRqwThreads) void requant_w_kernel(const uint4 *__restrict__ packed,
+                                                                const uint16_t *__restrict__ e4m3,
+                                                                float scale2,
+                                                                uint4 *__restrict__ q,
+                                                                float *__restrict__ scale,
+                                                                uint64_t nblocks) {
+    const uint64_t b = (uint64_t)blockIdx.x * kRqwThreads + threadIdx.x;
+    if (b >= nblocks) return;
+    const uint4 p = packed[b];
+    const uint32_t sc = e4m3[b];
+    const float s16[2] = {e4m3_to_f32(sc & 0xFFu), e4m3_to_f32(sc >> 8)};
+    const uint32_t mc[2] = {max_mag_code(p.x, p.y), max_mag_code(p.z, p.w)};
+
+    float amax = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) amax = fmaxf(amax, fabsf((e2m1_mag_to_f32(mc[h]) * s16[h]) * scale2));
+    const float s = amax / 127.0f;
+
+    uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+    if (s != 0.0f) {
+        const float mags[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+        uint32_t tab[2][4];  // pos_lo, pos_hi, neg_lo, neg_hi per half
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            int qm[8];
+            qm[0] = 0;
+#pragma unroll
+            for (int c = 1; c < 8; ++c) {
+                const float v = (mags[c] * s16[h]) * scale2;  // exact product, then one rounding
+                qm[c] = (int)fminf(fmaxf(rintf(v / s), -127.0f), 127.0f);
+            }
+            tab[h][0] = pack4_i8(qm[0], qm[1], qm[2], qm[3]);
+            tab[h][1] = pack4_i8(qm[4], qm[5], qm[6], qm[7]);
+            tab[h][2] = pack4_i8(-qm[0], -qm[1], -qm[2], -qm[3]);
+            tab[h][3] = pack4_i8(-qm[4], -qm[5], -qm[6], -qm[7]);
+        }
+        const uint2 e0 = lookup8(p.x, tab[0][0], tab[0][1], tab[0][2], tab[0][3]);
+        const uint2 e1 = lookup8(p.y, tab[0][0], tab[0][1], tab[0][2], tab[0][3]);
+        const uint2 e2 = lookup8(p.z, tab[1][0], tab[1][1], tab[1][2], tab[1][3]);
+        const uint2 e3 = lookup8(p.w, tab[1][0], tab[1][1], tab[1][2], tab[1][3]);
+        lo = make_uint4(e0.x, e0.y, e1.x, e1.y);
+        hi = make_uint4(e2.x, e2.y, e3.x, e3.y);
+    }
+    q[2 * b] = lo;
+    q[2 * b + 1] = hi;
+    scale[b] = s;
+}
+
+}  // namespace
+
+hipError_t launch_requant_a(const uint16_t *a_bf16, int8_t *a_i8, float *a_scale, uint64_t nblocks,
+                            hipStream_t s) {
+    const uint64_t nchunks = nblocks * kRqaLanesPerBlock;
+    const uint64_t grid = div_up(nchunks, kRqaThreads);
+    hipLaunchKernelGGL(requant_a_kernel, dim3((uint32_t)grid), dim3(kRqaThreads), 0, s,
+                       reinterpret_cast<const uint4 *>(a_bf16), reinterpret_cast<uint2 *>(a_i8),
+                       a_scale, nchunks);
+    return hipGetLastError();
+}
+
+hipError_t launch_requant_w(const uint8_t *w_packed, const uint8_t *w_e4m3, float scale2,
+                            int8_t *w_i8, float *w_scale, uint64_t nblocks, hipStream_t s) {
+    const uint64_t grid = div_up(nblocks, kRqwThreads);
+    hipLaunchKernelGGL(requant_w_kernel, dim3((uint32_t)grid), dim3(kRqwThreads), 0, s,
+                       reinterpret_cast<const uint4 *>(w_packed),
+                       reinterpret_cast<const uint16_t *>(w_e4m3), scale2,
+                       reinterpret_cast<uint4 *>(w_i8), w_scale, nblocks);
+    return hipGetLastError();
+}
+
+}  // namespace bsr

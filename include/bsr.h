@@ -1,0 +1,134 @@
+/*
+ * bsr.h -- C ABI of the MI355X (gfx950) block-scaled int8 projection library.
+ *
+ * The projection Y[M,N] = A[M,K] * W[N,K]^T runs in three steps, each one
+ * entry point below:
+ *   1. requant_w_nvfp4_int8  -- one-time: NVFP4 weight -> int8 + F32 per 32;
+ *   2. requant_a_int8        -- per call: BF16 activations -> int8 + F32 per 32;
+ *   3. int8_gemm_blockscaled -- int8 x int8 with an exact int32 dot product per
+ *      32-wide K block, each block rescaled in FP32 by a_scale * w_scale,
+ *      accumulated in FP32 and written as BF16 (an MFMA GEMM for M > 8, a
+ *      weight-streaming GEMV for M <= 8).
+ * The operations are those of page "metrale_model_layers/layers/ops/
+ * gemm_dense_int8.rs": the doc comments of `requant_w_nvfp4_int8` and
+ * `int8_gemm_faith2_prefill` (the latter's two launches are entry points 2
+ * and 3 here).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensors are dense row-major DEVICE buffers owned by the caller; the
+ *   library allocates nothing, keeps no pointer after it returns and never
+ *   synchronises.  Host pointers are not accepted (undefined behaviour).
+ * - Work is enqueued on `stream` (a hipStream_t passed as void*, NULL = the
+ *   default stream).  Calls on one stream run in order, so the output of
+ *   requant_a_int8 may be passed straight to int8_gemm_blockscaled.
+ * - Sizes are uint32_t; index arithmetic inside is 64-bit.
+ * - Validation happens before any launch: on an error nothing is launched and
+ *   no output byte is written.  There is no fallback to another path.
+ * - m == 0 or n == 0 is a valid empty problem: BSR_OK, nothing launched.
+ * - k must be a positive multiple of 32 (every K/2, K/16, K/32 is whole).
+ * - Inputs outside the method's contract (NaN/Inf activations, NaN E4M3
+ *   scale codes, a non-finite dequantized weight) give unspecified output.
+ * - Outputs must not alias inputs (undefined behaviour, not checked).
+ * - The calling thread's current HIP device must be a gfx950 GPU; the device
+ *   check is cached per device, so the library is safe to call from several
+ *   host threads.
+ *
+ * Number formats: E2M1 per the OCP Microscaling Formats v1.0 spec, element
+ * 2j of a packed byte row in the LOW nibble of byte j; E4M3 per the OCP 8-bit
+ * floating point spec (no infinities, S.1111.111 NaN); BF16 = upper half of
+ * an IEEE binary32.
+ *
+ * Quantizer (steps 1 and 2), per 32-element block of a row:
+ *   amax = max |v|;  s = fl32(amax / 127) (IEEE divide), stored as the scale;
+ *   s == 0 (zero block or underflow): scale +0.0f and q = 0;
+ *   else q = clamp(round_half_even(fl32(v / s)), -127, 127).
+ * Results are bit-identical to that definition (subnormals included).
+ */
+#ifndef BSR_H
+#define BSR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum bsr_status {
+    BSR_OK = 0,
+    BSR_EINVAL = 1,  /* k == 0, k % 32 != 0, unsupported size, or bad `path` */
+    BSR_ENULL = 2,   /* a required pointer is NULL (m, n > 0)                */
+    BSR_EALIGN = 3,  /* a pointer is not aligned as stated per argument      */
+    BSR_EDEVICE = 4, /* no current HIP device, or it is not gfx950           */
+    BSR_ELAUNCH = 5  /* the kernel launch reported an error                  */
+};
+
+/*
+ * Step 1, one-time weight requant (page ".../gemm_dense_int8.rs", doc of
+ * `requant_w_nvfp4_int8`).
+ *   w_packed [n, k/2]  u8  two E2M1 codes per byte, low nibble first; 16-byte aligned
+ *   w_e4m3   [n, k/16] u8  E4M3 scale of elements 16c..16c+15;       2-byte aligned
+ *   scale2             f32 per-tensor scale, by value; must be finite
+ *   w_i8     [n, k]    i8  output codes in [-127, 127];              16-byte aligned
+ *   w_scale  [n, k/32] f32 output scale of each 32-block;             4-byte aligned
+ * Dequantized value: v = fl32(fl32(e2m1 * e4m3) * scale2) (the first product
+ * is exact), then the quantizer above.
+ * Errors: BSR_EINVAL (k, or scale2 not finite), BSR_ENULL, BSR_EALIGN,
+ * BSR_EDEVICE, BSR_ELAUNCH.
+ */
+int requant_w_nvfp4_int8(const uint8_t *w_packed, const uint8_t *w_e4m3, float scale2,
+                         int8_t *w_i8, float *w_scale, uint32_t n, uint32_t k, void *stream);
+
+/*
+ * Step 2, per-call activation requant (page ".../gemm_dense_int8.rs", doc of
+ * `int8_gemm_faith2_prefill`, its first launch).
+ *   a_bf16  [m, k]    BF16 as raw u16;  16-byte aligned
+ *   a_i8    [m, k]    i8 output;        16-byte aligned (caller-owned scratch)
+ *   a_scale [m, k/32] f32 output;        4-byte aligned (caller-owned scratch)
+ * Errors: BSR_EINVAL, BSR_ENULL, BSR_EALIGN, BSR_EDEVICE, BSR_ELAUNCH.
+ */
+int requant_a_int8(const uint16_t *a_bf16, int8_t *a_i8, float *a_scale,
+                   uint32_t m, uint32_t k, void *stream);
+
+/*
+ * Step 3, block-scaled GEMM (page ".../gemm_dense_int8.rs", doc of
+ * `int8_gemm_faith2_prefill`, its second launch).
+ *   a_i8    [m, k]    i8,  16-byte aligned     w_i8    [n, k]    i8,  16-byte aligned
+ *   a_scale [m, k/32] f32,  4-byte aligned     w_scale [n, k/32] f32,  4-byte aligned
+ *   out     [m, n]    BF16 as raw u16, 2-byte aligned
+ * out[i,j] = bf16_rne( FP32 sum over blocks b of fl32(a_scale[i,b] * w_scale[j,b])
+ *            * P[i,j,b] ), P the exact int32 dot product of block b.  The FP32
+ * summation order is the kernel's own (not part of the contract); the result
+ * is within 4e-3 relative or 1 BF16 ulp of the FP64 value, or within the
+ * worst-case FP32 error of a K/32-term sum where that is larger.
+ * m <= 8 runs the weight-streaming GEMV, m > 8 the MFMA GEMM.
+ * Errors: BSR_EINVAL, BSR_ENULL, BSR_EALIGN, BSR_EDEVICE, BSR_ELAUNCH.
+ */
+int int8_gemm_blockscaled(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
+                          const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
+                          uint32_t k, void *stream);
+
+/* Paths of int8_gemm_blockscaled_ex. */
+enum bsr_path {
+    BSR_PATH_AUTO = 0, /* GEMV iff m <= 8, as int8_gemm_blockscaled     */
+    BSR_PATH_GEMM = 1, /* the MFMA GEMM at any m                         */
+    BSR_PATH_GEMV = 2  /* the GEMV; requires m <= 8, else BSR_EINVAL     */
+};
+
+/*
+ * int8_gemm_blockscaled with an explicit path, so tests can run both kernels
+ * on the same rows (same arguments and errors; BSR_EINVAL for an unknown path).
+ */
+int int8_gemm_blockscaled_ex(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
+                             const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
+                             uint32_t k, void *stream, int path);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *bsr_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSR_H */

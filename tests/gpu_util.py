@@ -1,0 +1,58 @@
+"""Device-side helpers for the GPU parity tests: move seeded numpy inputs to the
+GPU, run the library's entry points through the C ABI, bring results back."""
+import sys
+
+import numpy as np
+import torch
+
+from block_scaled_precision_requant_amd import bsr
+
+DEV = torch.device("cuda:0")
+
+
+def say(*args):
+    print(*args, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(arr):
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(DEV)
+
+
+def gpu_requant_w(packed, e4m3, scale2):
+    n, half_k = packed.shape
+    k = 2 * half_k
+    wp, we = to_dev(packed), to_dev(e4m3)
+    w_i8 = torch.empty((n, k), dtype=torch.int8, device=DEV)
+    w_s = torch.empty((n, k // 32), dtype=torch.float32, device=DEV)
+    bsr.requant_w_nvfp4_int8(wp, we, float(scale2), w_i8, w_s)
+    return w_i8, w_s
+
+
+def gpu_requant_a(a_bits):
+    a = to_dev(a_bits.view(np.int16))
+    m, k = a.shape
+    a_i8 = torch.empty((m, k), dtype=torch.int8, device=DEV)
+    a_s = torch.empty((m, k // 32), dtype=torch.float32, device=DEV)
+    bsr.requant_a_int8(a, a_i8, a_s)
+    return a_i8, a_s
+
+
+def gpu_gemm(a_i8, w_i8, a_s, w_s, path=bsr.PATH_AUTO):
+    m = a_i8.shape[0]
+    n = w_i8.shape[0]
+    out = torch.empty((m, n), dtype=torch.int16, device=DEV)
+    bsr.int8_gemm_blockscaled_ex(a_i8, w_i8, a_s, w_s, out, path=path)
+    return out
+
+
+def host(t):
+    torch.cuda.synchronize()
+    arr = t.cpu().numpy()
+    if arr.dtype == np.int16:
+        arr = arr.view(np.uint16)
+    return arr
+
+
+def f32_bits(x):
+    return np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)

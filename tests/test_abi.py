@@ -1,0 +1,92 @@
+"""The C-ABI library loads and exports every entry point include/bsr.h declares,
+and argument validation answers before any GPU work (CPU only: no kernel runs)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from block_scaled_precision_requant_amd import bsr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsr.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared_functions() == set(bsr.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", bsr.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = _declared_functions() - exported
+    assert not missing, missing
+    L = bsr.lib()
+    for name in _declared_functions():
+        assert getattr(L, name) is not None
+
+
+def test_status_strings():
+    for st in range(6):
+        assert bsr.status_string(st).startswith("BSR_")
+    assert "unknown" in bsr.status_string(99)
+
+
+FAKE = ctypes.c_void_p(1 << 20)       # never dereferenced: every call below fails validation first
+
+
+def _fake(off=0):
+    return ctypes.c_void_p((1 << 20) + off)
+
+
+def test_bad_k_is_rejected_before_anything_else():
+    L = bsr.lib()
+    for k in (0, 16, 48, 33):
+        assert L.requant_a_int8(FAKE, FAKE, FAKE, 4, k, None) == bsr.BSR_EINVAL
+        assert L.requant_w_nvfp4_int8(FAKE, FAKE, 1.0, FAKE, FAKE, 4, k, None) == bsr.BSR_EINVAL
+        assert L.int8_gemm_blockscaled(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, k, None) == bsr.BSR_EINVAL
+
+
+def test_empty_problems_are_noops():
+    L = bsr.lib()
+    null = ctypes.c_void_p(0)
+    assert L.requant_a_int8(null, null, null, 0, 64, None) == bsr.BSR_OK
+    assert L.requant_w_nvfp4_int8(null, null, 1.0, null, null, 0, 64, None) == bsr.BSR_OK
+    assert L.int8_gemm_blockscaled(null, null, null, null, null, 0, 7, 64, None) == bsr.BSR_OK
+    assert L.int8_gemm_blockscaled(null, null, null, null, null, 7, 0, 64, None) == bsr.BSR_OK
+
+
+def test_null_and_alignment_errors():
+    L = bsr.lib()
+    null = ctypes.c_void_p(0)
+    assert L.requant_a_int8(null, FAKE, FAKE, 4, 64, None) == bsr.BSR_ENULL
+    assert L.requant_a_int8(_fake(8), FAKE, FAKE, 4, 64, None) == bsr.BSR_EALIGN
+    assert L.requant_a_int8(FAKE, FAKE, _fake(2), 4, 64, None) == bsr.BSR_EALIGN
+    assert L.requant_w_nvfp4_int8(FAKE, _fake(1), 1.0, FAKE, FAKE, 4, 64, None) == bsr.BSR_EALIGN
+    assert L.requant_w_nvfp4_int8(FAKE, FAKE, 1.0, null, FAKE, 4, 64, None) == bsr.BSR_ENULL
+    assert L.int8_gemm_blockscaled(FAKE, _fake(4), FAKE, FAKE, FAKE, 4, 4, 64, None) == bsr.BSR_EALIGN
+    assert L.int8_gemm_blockscaled(FAKE, FAKE, FAKE, FAKE, _fake(1), 4, 4, 64, None) == bsr.BSR_EALIGN
+    assert L.int8_gemm_blockscaled(FAKE, FAKE, FAKE, FAKE, null, 4, 4, 64, None) == bsr.BSR_ENULL
+
+
+def test_bad_scale2_and_path():
+    L = bsr.lib()
+    for s2 in (float("nan"), float("inf"), -float("inf")):
+        assert L.requant_w_nvfp4_int8(FAKE, FAKE, s2, FAKE, FAKE, 4, 64, None) == bsr.BSR_EINVAL
+    assert L.int8_gemm_blockscaled_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 64, None, 3) == bsr.BSR_EINVAL
+    assert L.int8_gemm_blockscaled_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 9, 4, 64, None,
+                                      bsr.PATH_GEMV) == bsr.BSR_EINVAL
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU may be present")
+def test_no_device_is_reported():
+    L = bsr.lib()
+    assert L.requant_a_int8(FAKE, FAKE, FAKE, 4, 64, None) == bsr.BSR_EDEVICE

@@ -1,0 +1,146 @@
+"""GPU parity of the two quantizers: bit-exact against the CPU oracle on every
+workload's full tensors and on exhaustive value sweeps."""
+import numpy as np
+import pytest
+
+import oracle
+from block_scaled_precision_requant_amd import inputs
+from gpu_util import f32_bits, gpu_requant_a, gpu_requant_w, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _assert_same(name, q_gpu, s_gpu, q_ref, s_ref):
+    assert q_gpu.shape == q_ref.shape and s_gpu.shape == s_ref.shape, name
+    bad_s = np.argwhere(f32_bits(s_gpu) != f32_bits(s_ref))
+    assert bad_s.size == 0, f"{name}: {len(bad_s)} scale mismatches, first {bad_s[0]}"
+    bad_q = np.argwhere(q_gpu != q_ref)
+    assert bad_q.size == 0, f"{name}: {len(bad_q)} code mismatches, first {bad_q[0]}"
+
+
+def _projections():
+    out = []
+    seen = set()
+    for w in inputs.workloads():
+        for p in w.projections:
+            key = (p.seed, p.tensor_base, p.n, p.k)
+            if key not in seen:
+                seen.add(key)
+                out.append(p)
+    return out
+
+
+@pytest.mark.parametrize("proj", _projections(), ids=lambda p: p.name)
+def test_requant_w_workload_bitexact(proj):
+    say(f"requant_w {proj.name} n={proj.n} k={proj.k}")
+    packed, e4m3 = proj.weight()
+    q_ref, s_ref = oracle.requant_w(packed, e4m3, proj.scale2)
+    q, s = gpu_requant_w(packed, e4m3, proj.scale2)
+    _assert_same(proj.name, host(q), host(s), q_ref, s_ref)
+
+
+def _a_projections():
+    out = []
+    for w in inputs.workloads():
+        for p in w.projections:
+            out.append(p)
+    return out
+
+
+@pytest.mark.parametrize("proj", _a_projections(), ids=lambda p: p.name)
+def test_requant_a_workload_bitexact(proj):
+    say(f"requant_a {proj.name} m={proj.m} k={proj.k}")
+    a = proj.activations()
+    q_ref, s_ref = oracle.requant_a(a)
+    q, s = gpu_requant_a(a)
+    _assert_same(proj.name, host(q), host(s), q_ref, s_ref)
+
+
+def _pair_blocks(amax_bits, v_lo):
+    """Blocks [amax, v1..v31] covering every BF16 v in [v_lo, amax] for each amax."""
+    blocks = []
+    for a in amax_bits:
+        vs = np.arange(v_lo, a + 1, dtype=np.uint32).astype(np.uint16)
+        vs[1::2] |= 0x8000                       # alternate signs
+        pad = (-len(vs)) % 31
+        vs = np.concatenate([vs, np.zeros(pad, np.uint16)]).reshape(-1, 31)
+        blk = np.empty((vs.shape[0], 32), np.uint16)
+        blk[:, 0] = a
+        blk[:, 1:] = vs
+        blocks.append(blk)
+    return np.concatenate(blocks)
+
+
+@pytest.mark.parametrize("exp", [-100, -20, -1, 0, 1, 20, 100])
+def test_requant_a_exhaustive_binade(exp):
+    # Every BF16 amax of the binade [2^exp, 2^(exp+1)) with every v in [amax*2^-9, amax].
+    lo_bits = (exp + 127) << 7
+    amax = np.arange(lo_bits, lo_bits + 128, dtype=np.uint32)
+    v_lo = max(1, lo_bits - (9 << 7))
+    blocks = _pair_blocks(amax, v_lo)
+    say(f"requant_a binade 2^{exp}: {blocks.shape[0]} blocks")
+    a = blocks.reshape(-1, 1024) if blocks.size % 1024 == 0 else blocks.reshape(1, -1)
+    q_ref, s_ref = oracle.requant_a(a)
+    q, s = gpu_requant_a(a)
+    _assert_same(f"binade {exp}", host(q), host(s), q_ref, s_ref)
+
+
+def test_requant_a_exhaustive_subnormal_scales():
+    # Every amax whose scale amax/127 is a binary32 subnormal, with every v <= amax.
+    amax = np.arange(1, 0x0400, dtype=np.uint32)
+    blocks = _pair_blocks(amax, 0)
+    say(f"requant_a subnormal scales: {blocks.shape[0]} blocks")
+    a = blocks.reshape(1, -1)
+    q_ref, s_ref = oracle.requant_a(a)
+    q, s = gpu_requant_a(a)
+    _assert_same("subnormal", host(q), host(s), q_ref, s_ref)
+
+
+def test_requant_a_zero_and_special_blocks():
+    a = np.zeros((3, 128), np.uint16)
+    a[0, 32:64] = 0x8000                            # -0 block
+    a[1, 64] = 0x0001                               # smallest subnormal alone
+    a[2, :32] = 0x3F80                              # all equal
+    a[2, 96:] = np.arange(32, dtype=np.uint16) | 0x4200
+    q_ref, s_ref = oracle.requant_a(a)
+    q, s = gpu_requant_a(a)
+    _assert_same("special", host(q), host(s), q_ref, s_ref)
+    assert f32_bits(host(s))[0, 1] == 0
+
+
+@pytest.mark.parametrize("scale2", [np.float32(1 / 64), inputs.SCALE2_1_448, np.float32(0.0123456),
+                                    np.float32(-3.0e-3), np.float32(1e-38)])
+def test_requant_w_exhaustive_scale_pairs(scale2):
+    # Every pair of finite positive E4M3 codes (sa, sb) on the two halves, each half
+    # holding all 16 E2M1 codes; plus negative scale codes.
+    codes = [c for c in range(0x01, 0x7F)]
+    sa, sb = np.meshgrid(codes, codes, indexing="ij")
+    pairs = np.stack([sa.ravel(), sb.ravel()], axis=1)
+    neg = pairs[::97] | 0x80
+    pairs = np.concatenate([pairs, neg]).astype(np.uint8)
+    nib = np.arange(16, dtype=np.uint8)
+    half = (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8)
+    rng = np.random.default_rng(int(scale2.view(np.uint32)) & 0xFFFF)
+    packed = np.tile(np.concatenate([half, half]), (pairs.shape[0], 1))
+    # shuffle the bytes within each half per row so the code -> position map varies
+    rows = pairs.shape[0]
+    perm = np.concatenate([rng.permuted(np.tile(np.arange(8), (rows, 1)), axis=1),
+                           8 + rng.permuted(np.tile(np.arange(8), (rows, 1)), axis=1)], axis=1)
+    packed = np.take_along_axis(packed, perm, axis=1)
+    say(f"requant_w pairs scale2={float(scale2)}: {pairs.shape[0]} rows")
+    q_ref, s_ref = oracle.requant_w(packed, pairs, scale2)
+    q, s = gpu_requant_w(packed, pairs, scale2)
+    _assert_same(f"pairs {float(scale2)}", host(q), host(s), q_ref, s_ref)
+
+
+def test_requant_w_random_codes_and_sparse_blocks():
+    rng = np.random.default_rng(123)
+    n, k = 777, 2048
+    packed = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    packed[::5, :16] = 0x88                          # -0 everywhere: zero block
+    packed[1::7, 16:32] &= 0x99                      # only codes 0, 1, 8, 9
+    e4m3 = rng.integers(0, 0x7F, size=(n, k // 16), dtype=np.uint8)   # finite codes incl. 0 and subnormals
+    for s2 in (inputs.SCALE2_1_448, np.float32(2.0 ** -120)):
+        q_ref, s_ref = oracle.requant_w(packed, e4m3, s2)
+        q, s = gpu_requant_w(packed, e4m3, s2)
+        _assert_same(f"random {float(s2)}", host(q), host(s), q_ref, s_ref)
