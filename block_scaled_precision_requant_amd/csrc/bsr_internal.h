@@ -19,14 +19,18 @@ constexpr int kRqwThreads = 256;
 
 // ---- GEMM (m > 8) ---------------------------------------------------------
 // A workgroup of 4 waves computes a kGemmBM x kGemmBN output tile; each wave
-// owns a 64 x 64 quarter as 2 x 2 MFMA 32x32x32 int8 tiles.  The K loop
-// stages kGemmStageBlocks 32-wide blocks of A and W per LDS pass.
+// owns a 64 x 64 quarter as 2 x 2 MFMA 32x32 tiles.  The K loop stages
+// kGemmStageBlocks 32-wide blocks of A, W and their scales per LDS buffer,
+// in a ring of kGemmRing buffers.  Workgroups are ordered so that each XCD runs a compact
+// kGemmGroupM-tall group of output tiles.
 constexpr int kGemmThreads = 256;
 constexpr int kGemmBM = 128;
 constexpr int kGemmBN = 128;
 constexpr int kGemmStageBlocks = 4;
-constexpr int kGemmStageBytes = 32 * kGemmStageBlocks;   // 128 bytes of K per row
-constexpr int kGemmLdsRowStride = kGemmStageBytes + 16;   // pad: rows start 4 banks apart
+constexpr int kGemmStageBytes = 32 * kGemmStageBlocks;    // 128 bytes of K per row: whole cache lines
+constexpr int kGemmRing = 2;                              // stage buffers in flight
+constexpr int kGemmGroupM = 8;
+constexpr int kXcds = 8;
 
 // ---- GEMV (m <= 8) --------------------------------------------------------
 // kGemvLanesPerCol lanes split the K blocks of one output column; a wave

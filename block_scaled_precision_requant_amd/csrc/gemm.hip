@@ -5,12 +5,18 @@
 // `int8_gemm_faith2_prefill` on page "metrale_model_layers/layers/ops/
 // gemm_dense_int8.rs".
 //
-// One v_mfma_i32_32x32x32_i8 covers exactly one scale block of a 32 x 32
-// output tile, so each block's P leaves the matrix core as int32 and is
-// rescaled into FP32 accumulators in registers before the next block.
-// A and W tiles of kGemmStageBlocks blocks are staged through LDS (rows padded
-// so 8 consecutive rows start on distinct bank groups); the scales are staged
-// transposed so a lane's four consecutive output rows read one 16-byte word.
+// Matrix-core work per 32 x 32 output tile and pair of K blocks:
+//   * two v_mfma_i32_32x32x32_i8, each one whole scale block -> exact P;
+//   * one v_mfma_f32_32x32x1_2b_f32, the outer products a_s x w_s of both
+//     blocks (a single product per output, so each is fl32(a_s * w_s)).
+// What is left for the vector ALU is one int -> float conversion and one FMA
+// per output and block.
+//
+// Operand staging: a stage is kGemmStageBlocks blocks (128 bytes of every A
+// and W row, i.e. whole cache lines) plus the matching scales, copied straight
+// from global memory into LDS with global_load_lds (no registers held while
+// the copy is in flight) into a ring of kGemmRing buffers; the next stage is
+// in flight while the current one is computed, with one barrier per stage.
 #include "bsr_internal.h"
 
 namespace bsr {
@@ -18,24 +24,143 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v32f __attribute__((ext_vector_type(32)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kChunksPerRow = kGemmStageBytes / 16;                          // 8
+constexpr int kRowsPerCopy = 64 / kChunksPerRow;                             // 8 rows per 1 KB wave copy
+constexpr int kWaves = kGemmThreads / 64;                                    // 4
+constexpr int kTileCopiesPerWave = kGemmBM / (kRowsPerCopy * kWaves);        // 4
+constexpr int kTileBytes = kGemmBM * kGemmStageBytes;                        // 16 KB
+constexpr int kScaleFloats = kGemmBM * kGemmStageBlocks;                     // 512 per operand
+constexpr int kScaleCopiesPerWave = kScaleFloats / (64 * kWaves);            // 2
+static_assert(kGemmBM == kGemmBN, "square tiles assumed by the loaders");
+static_assert(kChunksPerRow == 8, "the chunk swizzle permutes 8 chunks per row");
+static_assert(kGemmStageBlocks % 2 == 0, "the 2-block f32 MFMA covers pairs of blocks");
+static_assert(kGemmRing == 2, "the loop below alternates two buffers");
+
+// Workgroup -> output tile.  Workgroups are dispatched round-robin over the
+// XCDs; renumber them so each XCD gets a contiguous run, then walk the runs in
+// groups of kGemmGroupM tile rows so an XCD's concurrent tiles share A and W
+// rows in its L2.
+__device__ __forceinline__ void tile_of(uint32_t wg, uint32_t tiles_m, uint32_t tiles_n,
+                                        uint32_t &tm, uint32_t &tn) {
+    const uint32_t total = tiles_m * tiles_n;
+    const uint32_t q = total / kXcds, r = total % kXcds;
+    const uint32_t x = wg % kXcds, j = wg / kXcds;
+    const uint32_t v = x * q + min(x, r) + j;
+    const uint32_t per_group = kGemmGroupM * tiles_n;
+    const uint32_t first_m = (v / per_group) * kGemmGroupM;
+    const uint32_t gsize = min(tiles_m - first_m, (uint32_t)kGemmGroupM);
+    const uint32_t in_group = v % per_group;
+    tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+}
+
+// LDS rows are 128 bytes with no padding; 16-byte chunk c of row r sits at
+// slot c ^ swz(r).  Eight consecutive rows read at one chunk then hit eight
+// distinct slots, and sixteen consecutive rows hit distinct (row parity, slot)
+// pairs, so a 64-lane ds_read_b128 is conflict-free on 32- or 64-bank LDS.
+__device__ __forceinline__ uint32_t chunk_swz(uint32_t r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+struct Stage {
+    int8_t a[kTileBytes];
+    int8_t w[kTileBytes];
+    float as[kGemmBM][kGemmStageBlocks];  // [row][block of the stage]
+    float ws[kGemmBN][kGemmStageBlocks];
+};
+
+// Issue one stage's global -> LDS copies.  A wave's copy fills LDS in lane
+// order (16 or 4 bytes per lane); the lane whose LDS slot is (row, slot)
+// fetches chunk slot ^ swz(row).  Rows past M or N re-read the last row (their
+// outputs are never stored); K chunks and scale blocks past the last block
+// re-read the last one, and the compute zeroes the scale product of any block
+// past K.  Scale copies map consecutive lanes to consecutive blocks of a row,
+// so one copy touches 16 rows' worth of contiguous bytes.
+__device__ __forceinline__ void issue_stage(Stage &st, const int8_t *a, const int8_t *w,
+                                            const float *a_s, const float *w_s, uint32_t M,
+                                            uint32_t N, uint32_t K, uint32_t nb, uint32_t m0,
+                                            uint32_t n0, uint32_t kb, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < kTileCopiesPerWave; ++i) {
+        const int seg = i * kWaves + wave;                       // 1 KB segment of the tile
+        const uint32_t row = seg * kRowsPerCopy + lane / kChunksPerRow;
+        const uint32_t chunk = (lane % kChunksPerRow) ^ chunk_swz(row);
+        const uint64_t kof = min((uint64_t)kb * 32 + chunk * 16, (uint64_t)K - 16);
+        __builtin_amdgcn_global_load_lds(a + (uint64_t)min(m0 + row, M - 1) * K + kof,
+                                         (lds_void *)(st.a + seg * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(w + (uint64_t)min(n0 + row, N - 1) * K + kof,
+                                         (lds_void *)(st.w + seg * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kScaleCopiesPerWave; ++i) {
+        const int seg = i * kWaves + wave;                       // 64 floats of the scale tile
+        const uint32_t idx = seg * 64 + lane;                    // = row * kGemmStageBlocks + block
+        const uint32_t row = idx / kGemmStageBlocks;
+        const uint32_t blk = min(kb + idx % kGemmStageBlocks, nb - 1);
+        __builtin_amdgcn_global_load_lds(a_s + (uint64_t)min(m0 + row, M - 1) * nb + blk,
+                                         (lds_void *)(&st.as[0][0] + seg * 64), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(w_s + (uint64_t)min(n0 + row, N - 1) * nb + blk,
+                                         (lds_void *)(&st.ws[0][0] + seg * 64), 4, 0, 0);
+    }
+}
+
+// Wait until at most n of this wave's global -> LDS copies are outstanding.
+// Copies complete in issue order, so this waits for every older stage.
+// (s_waitcnt on gfx9: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt
+// 11:8 left at their maxima.)
+template <int n>
+__device__ __forceinline__ void wait_copies() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// those would wait for every copy in flight (vmcnt(0)) and drain the ring.
+// Visibility is handled explicitly: copies are waited for with wait_copies()
+// before the barrier, and a wave's LDS reads of a stage have returned before
+// its compute (which consumes them) ends.  The memory clobber keeps the
+// compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Empty asm that reads and "writes" 16 accumulators: the compiler must finish
+// the FMAs feeding them before this point, so a stage's compute cannot drift
+// past the following wait-for-copies and barrier.
+#define BSR_PIN16(x)                                                                         \
+    asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), \
+                 "+v"(x[6]), "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]),    \
+                 "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15]))
 
 __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(
     const int8_t *__restrict__ a, const int8_t *__restrict__ w, const float *__restrict__ a_s,
     const float *__restrict__ w_s, uint16_t *__restrict__ out, uint32_t M, uint32_t N, uint32_t K,
-    uint32_t tiles_n) {
-    __shared__ __attribute__((aligned(16))) int8_t lds_a[kGemmBM * kGemmLdsRowStride];
-    __shared__ __attribute__((aligned(16))) int8_t lds_w[kGemmBN * kGemmLdsRowStride];
-    __shared__ __attribute__((aligned(16))) float lds_as[kGemmStageBlocks][kGemmBM];
-    __shared__ __attribute__((aligned(16))) float lds_ws[kGemmStageBlocks][kGemmBN];
+    uint32_t tiles_m, uint32_t tiles_n) {
+    __shared__ __attribute__((aligned(1024))) Stage ring[kGemmRing];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const uint32_t tile = blockIdx.x;
-    const uint32_t m0 = (tile / tiles_n) * kGemmBM;
-    const uint32_t n0 = (tile % tiles_n) * kGemmBN;
+    uint32_t tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const uint32_t m0 = tm * kGemmBM, n0 = tn * kGemmBN;
     const uint32_t nb = K / 32;
+    const uint32_t nstages = (nb + kGemmStageBlocks - 1) / kGemmStageBlocks;
+
+    // Per-lane LDS offsets of the MFMA operands (constant over the K loop):
+    // lane l reads row (l % 32) of its 32-row tile and, for block j, the 16-byte
+    // half (l / 32) of it.
+    const uint32_t sw = chunk_swz(lane & 31);
+    const int half = lane >> 5;
+    int off_a[2][kGemmStageBlocks], off_w[2][kGemmStageBlocks];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < kGemmStageBlocks; ++j) {
+            const int chunk = 2 * j + half;
+            off_a[t][j] = (wm * 64 + t * 32 + (lane & 31)) * kGemmStageBytes + ((chunk ^ sw) << 4);
+            off_w[t][j] = (wn * 64 + t * 32 + (lane & 31)) * kGemmStageBytes + ((chunk ^ sw) << 4);
+        }
 
     float acc[2][2][16];
 #pragma unroll
@@ -45,86 +170,79 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const v16i zero = {};
-    constexpr int kChunksPerRow = kGemmStageBytes / 16;                       // 8
-    constexpr int kChunkIters = kGemmBM * kChunksPerRow / kGemmThreads;       // 4
-    constexpr int kScaleIters = kGemmBM * kGemmStageBlocks / kGemmThreads;    // 2
+    const v16i zero16 = {};
+    const v32f zero32 = {};
 
-    for (uint32_t kb = 0; kb < nb; kb += kGemmStageBlocks) {
-        const uint32_t nbs = min((uint32_t)kGemmStageBlocks, nb - kb);
-        uint4 ra[kChunkIters], rw[kChunkIters];
-        float rsa[kScaleIters], rsw[kScaleIters];
+    // A block pair (blocks jp, jp + 1 of the stage) = 8 units (tile t = 2 sm + sn,
+    // block j).  The matrix-core result of unit u + 1 (and the scale products of
+    // its tile) is requested before unit u is rescaled, so each rescale reads a
+    // result that finished while the previous unit's 32 VALU instructions ran.
+    auto pair = [&](const Stage &cur, uint32_t kb, int jp) {
+        v4i af[2][2], bf[2][2];
+        float asv[2], wsv[2];
+        // lanes 0-31 carry block jp, lanes 32-63 block jp + 1 (zero if past K)
+        const bool blk_live = kb + jp + half < nb;
 #pragma unroll
-        for (int i = 0; i < kChunkIters; ++i) {
-            const int c = tid + kGemmThreads * i;
-            const int row = c / kChunksPerRow, col = c % kChunksPerRow;
-            const bool on = (uint32_t)col < 2 * nbs;
-            const uint64_t ga = (uint64_t)min(m0 + row, M - 1) * K + (uint64_t)kb * 32 + col * 16;
-            const uint64_t gw = (uint64_t)min(n0 + row, N - 1) * K + (uint64_t)kb * 32 + col * 16;
-            ra[i] = on ? *reinterpret_cast<const uint4 *>(a + ga) : make_uint4(0, 0, 0, 0);
-            rw[i] = on ? *reinterpret_cast<const uint4 *>(w + gw) : make_uint4(0, 0, 0, 0);
-        }
+        for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int i = 0; i < kScaleIters; ++i) {
-            const int idx = tid + kGemmThreads * i;
-            const int row = idx / kGemmStageBlocks, jb = idx % kGemmStageBlocks;
-            const bool on = (uint32_t)jb < nbs;
-            rsa[i] = on ? a_s[(uint64_t)min(m0 + row, M - 1) * nb + kb + jb] : 0.0f;
-            rsw[i] = on ? w_s[(uint64_t)min(n0 + row, N - 1) * nb + kb + jb] : 0.0f;
-        }
-        __syncthreads();  // the previous stage's readers are done
-#pragma unroll
-        for (int i = 0; i < kChunkIters; ++i) {
-            const int c = tid + kGemmThreads * i;
-            const int row = c / kChunksPerRow, col = c % kChunksPerRow;
-            *reinterpret_cast<uint4 *>(lds_a + row * kGemmLdsRowStride + col * 16) = ra[i];
-            *reinterpret_cast<uint4 *>(lds_w + row * kGemmLdsRowStride + col * 16) = rw[i];
-        }
-#pragma unroll
-        for (int i = 0; i < kScaleIters; ++i) {
-            const int idx = tid + kGemmThreads * i;
-            const int row = idx / kGemmStageBlocks, jb = idx % kGemmStageBlocks;
-            lds_as[jb][row] = rsa[i];
-            lds_ws[jb][row] = rsw[i];
-        }
-        __syncthreads();
-
-        for (uint32_t j = 0; j < nbs; ++j) {
-            v4i af[2], bf[2];
-            float wsv[2];
-            float asv[2][16];
-#pragma unroll
-            for (int sm = 0; sm < 2; ++sm) {
-                const int row = wm * 64 + sm * 32 + (lane & 31);
-                af[sm] = *reinterpret_cast<const v4i *>(lds_a + row * kGemmLdsRowStride + j * 32 +
-                                                        (lane >> 5) * 16);
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const float4 f = *reinterpret_cast<const float4 *>(
-                        &lds_as[j][wm * 64 + sm * 32 + 8 * g + 4 * (lane >> 5)]);
-                    asv[sm][4 * g + 0] = f.x;
-                    asv[sm][4 * g + 1] = f.y;
-                    asv[sm][4 * g + 2] = f.z;
-                    asv[sm][4 * g + 3] = f.w;
-                }
+            for (int j = 0; j < 2; ++j) {
+                af[t][j] = *reinterpret_cast<const v4i *>(cur.a + off_a[t][jp + j]);
+                bf[t][j] = *reinterpret_cast<const v4i *>(cur.w + off_w[t][jp + j]);
             }
-#pragma unroll
-            for (int sn = 0; sn < 2; ++sn) {
-                const int row = wn * 64 + sn * 32 + (lane & 31);
-                bf[sn] = *reinterpret_cast<const v4i *>(lds_w + row * kGemmLdsRowStride + j * 32 +
-                                                        (lane >> 5) * 16);
-                wsv[sn] = lds_ws[j][row];
-            }
-#pragma unroll
-            for (int sm = 0; sm < 2; ++sm)
-#pragma unroll
-                for (int sn = 0; sn < 2; ++sn) {
-                    const v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[sm], bf[sn], zero, 0, 0, 0);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        acc[sm][sn][r] = fmaf((float)p[r], asv[sm][r] * wsv[sn], acc[sm][sn][r]);
-                }
+            const float av = cur.as[wm * 64 + t * 32 + (lane & 31)][jp + half];
+            asv[t] = blk_live ? av : 0.0f;
+            wsv[t] = cur.ws[wn * 64 + t * 32 + (lane & 31)][jp + half];
         }
+        v32f sc[2];
+        v16i p[2];
+        sc[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(asv[0], wsv[0], zero32, 0, 0, 0);
+        p[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[0][0], bf[0][0], zero16, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int t = u >> 1, j = u & 1;
+            if (u + 1 < 8) {
+                const int t1 = (u + 1) >> 1, j1 = (u + 1) & 1;
+                if (j1 == 0)
+                    sc[t1 & 1] = __builtin_amdgcn_mfma_f32_32x32x1f32(asv[t1 >> 1], wsv[t1 & 1], zero32, 0, 0, 0);
+                p[(u + 1) & 1] =
+                    __builtin_amdgcn_mfma_i32_32x32x32_i8(af[t1 >> 1][j1], bf[t1 & 1][j1], zero16, 0, 0, 0);
+            }
+            float *ac = acc[t >> 1][t & 1];
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                ac[r] = fmaf((float)p[u & 1][r], sc[t & 1][16 * j + r], ac[r]);
+        }
+    };
+    auto compute = [&](const Stage &cur, uint32_t kb) {
+#pragma unroll
+        for (int jp = 0; jp < kGemmStageBlocks; jp += 2) {
+            pair(cur, kb, jp);
+            // read the next pair's operands only after this pair: bounds live registers
+            asm volatile("" ::: "memory");
+        }
+        BSR_PIN16(acc[0][0]);
+        BSR_PIN16(acc[0][1]);
+        BSR_PIN16(acc[1][0]);
+        BSR_PIN16(acc[1][1]);
+    };
+    auto issue = [&](Stage &buf, uint32_t stage) {
+        issue_stage(buf, a, w, a_s, w_s, M, N, K, nb, m0, n0, stage * kGemmStageBlocks, wave, lane);
+    };
+    // Stage s lives in buffer s % 2.  At the top of stage s each wave waits for
+    // its own copies of stage s, the barrier publishes every wave's copies and
+    // frees the other buffer (its stage s - 1 reads are done), and the copies of
+    // stage s + 1 go out before stage s is computed.
+    auto step = [&](Stage &cur, Stage &next, uint32_t s) {
+        wait_copies<0>();
+        stage_barrier();
+        if (s + 1 < nstages) issue(next, s + 1);
+        compute(cur, s * kGemmStageBlocks);
+    };
+    issue(ring[0], 0);
+    for (uint32_t s = 0; s < nstages; s += 2) {
+        step(ring[0], ring[1], s);
+        if (s + 1 >= nstages) break;
+        step(ring[1], ring[0], s + 1);
     }
 
     // Output layout of a 32x32 MFMA tile: lane l holds column l % 32 and, in
@@ -150,7 +268,7 @@ hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_sc
     const uint32_t tiles_m = (uint32_t)div_up(m, kGemmBM);
     const uint32_t tiles_n = (uint32_t)div_up(n, kGemmBN);
     hipLaunchKernelGGL(gemm_kernel, dim3(tiles_m * tiles_n), dim3(kGemmThreads), 0, s, a_i8, w_i8,
-                       a_scale, w_scale, out, m, n, k, tiles_n);
+                       a_scale, w_scale, out, m, n, k, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
