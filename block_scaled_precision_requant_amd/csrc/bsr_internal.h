@@ -18,13 +18,15 @@ constexpr int kRqaLanesPerBlock = 4;
 constexpr int kRqwThreads = 256;
 
 // ---- GEMM (m > 8) ---------------------------------------------------------
-// A workgroup of 4 waves computes a kGemmBM x kGemmBN output tile; each wave
-// owns a 64 x 64 quarter as 2 x 2 MFMA 32x32 tiles.  The K loop stages
-// kGemmStageBlocks 32-wide blocks of A, W and their scales per LDS buffer,
-// in a ring of kGemmRing buffers.  Workgroups are ordered so that each XCD runs a compact
-// kGemmGroupM-tall group of output tiles.
-constexpr int kGemmThreads = 256;
-constexpr int kGemmBM = 128;
+// A workgroup computes a BM x BN output tile with (BM/64) x (BN/64) waves, each
+// owning a 64 x 64 piece as 2 x 2 MFMA 32x32 tiles.  The K loop stages
+// kGemmStageBlocks 32-wide blocks of A, W and their scales per LDS buffer, in
+// a ring of kGemmRing buffers.  Workgroups are ordered so that each XCD runs a
+// compact kGemmGroupM-tall group of output tiles.  Two tile shapes are built:
+// 256 x 128 (8 waves, the default) and 128 x 128 (4 waves, for m <= 128).
+constexpr int kGemmWaveTile = 64;
+constexpr int kGemmBMLarge = 256;
+constexpr int kGemmBMSmall = 128;
 constexpr int kGemmBN = 128;
 constexpr int kGemmStageBlocks = 4;
 constexpr int kGemmStageBytes = 32 * kGemmStageBlocks;    // 128 bytes of K per row: whole cache lines
@@ -33,12 +35,15 @@ constexpr int kGemmGroupM = 8;
 constexpr int kXcds = 8;
 
 // ---- GEMV (m <= 8) --------------------------------------------------------
-// kGemvLanesPerCol lanes split the K blocks of one output column; a wave
-// covers 64 / kGemvLanesPerCol columns, a workgroup kGemvThreads / kGemvLanesPerCol.
-constexpr int kGemvThreads = 256;
-constexpr int kGemvLanesPerCol = 16;
-constexpr int kGemvColsPerWg = kGemvThreads / kGemvLanesPerCol;
+// A workgroup owns kGemvCols output columns and splits K over its waves; each
+// wave runs v_mfma_i32_16x16x64_i8 on (activation rows padded to 16) x (16
+// weight rows), one 64-byte K step at a time, the two 32-wide blocks of a step
+// separated by zeroing half of the activation operand.  The waves' FP32
+// partial sums are added in LDS in a fixed order.
+constexpr int kGemvCols = 16;
+constexpr int kGemvMaxWaves = 16;
 constexpr int kGemvMaxRows = 8;
+constexpr int kGemvBlocksPerIter = 4;   // K blocks per loop iteration of a wave (two MFMA steps)
 
 inline uint64_t div_up(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 

@@ -27,17 +27,28 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v32f __attribute__((ext_vector_type(32)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kChunksPerRow = kGemmStageBytes / 16;                          // 8
-constexpr int kRowsPerCopy = 64 / kChunksPerRow;                             // 8 rows per 1 KB wave copy
-constexpr int kWaves = kGemmThreads / 64;                                    // 4
-constexpr int kTileCopiesPerWave = kGemmBM / (kRowsPerCopy * kWaves);        // 4
-constexpr int kTileBytes = kGemmBM * kGemmStageBytes;                        // 16 KB
-constexpr int kScaleFloats = kGemmBM * kGemmStageBlocks;                     // 512 per operand
-constexpr int kScaleCopiesPerWave = kScaleFloats / (64 * kWaves);            // 2
-static_assert(kGemmBM == kGemmBN, "square tiles assumed by the loaders");
+constexpr int kChunksPerRow = kGemmStageBytes / 16;   // 8
+constexpr int kRowsPerCopy = 64 / kChunksPerRow;      // 8 rows per 1 KB wave copy
 static_assert(kChunksPerRow == 8, "the chunk swizzle permutes 8 chunks per row");
 static_assert(kGemmStageBlocks % 2 == 0, "the 2-block f32 MFMA covers pairs of blocks");
 static_assert(kGemmRing == 2, "the loop below alternates two buffers");
+
+// Geometry of one tile shape.
+template <int BM, int BN>
+struct Geo {
+    static constexpr int kWavesM = BM / kGemmWaveTile, kWavesN = BN / kGemmWaveTile;
+    static constexpr int kWaves = kWavesM * kWavesN;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kACopies = BM / (kRowsPerCopy * kWaves);            // 1 KB copies per wave
+    static constexpr int kWCopies = BN / (kRowsPerCopy * kWaves);
+    static constexpr int kASCopies = BM * kGemmStageBlocks / (64 * kWaves);  // 64-float copies per wave
+    static constexpr int kWSCopies = BN * kGemmStageBlocks / (64 * kWaves);
+    static_assert(kACopies * kRowsPerCopy * kWaves == BM && kWCopies * kRowsPerCopy * kWaves == BN,
+                  "tile rows split evenly over the waves' copies");
+    static_assert(kASCopies * 64 * kWaves == BM * kGemmStageBlocks &&
+                      kWSCopies * 64 * kWaves == BN * kGemmStageBlocks,
+                  "scale tiles split evenly over the waves' copies");
+};
 
 // Workgroup -> output tile.  Workgroups are dispatched round-robin over the
 // XCDs; renumber them so each XCD gets a contiguous run, then walk the runs in
@@ -63,11 +74,12 @@ __device__ __forceinline__ void tile_of(uint32_t wg, uint32_t tiles_m, uint32_t 
 // pairs, so a 64-lane ds_read_b128 is conflict-free on 32- or 64-bank LDS.
 __device__ __forceinline__ uint32_t chunk_swz(uint32_t r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+template <int BM, int BN>
 struct Stage {
-    int8_t a[kTileBytes];
-    int8_t w[kTileBytes];
-    float as[kGemmBM][kGemmStageBlocks];  // [row][block of the stage]
-    float ws[kGemmBN][kGemmStageBlocks];
+    int8_t a[BM * kGemmStageBytes];
+    int8_t w[BN * kGemmStageBytes];
+    float as[BM][kGemmStageBlocks];  // [row][block of the stage]
+    float ws[BN][kGemmStageBlocks];
 };
 
 // Issue one stage's global -> LDS copies.  A wave's copy fills LDS in lane
@@ -77,31 +89,47 @@ struct Stage {
 // re-read the last one, and the compute zeroes the scale product of any block
 // past K.  Scale copies map consecutive lanes to consecutive blocks of a row,
 // so one copy touches 16 rows' worth of contiguous bytes.
-__device__ __forceinline__ void issue_stage(Stage &st, const int8_t *a, const int8_t *w,
-                                            const float *a_s, const float *w_s, uint32_t M,
-                                            uint32_t N, uint32_t K, uint32_t nb, uint32_t m0,
-                                            uint32_t n0, uint32_t kb, int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < kTileCopiesPerWave; ++i) {
-        const int seg = i * kWaves + wave;                       // 1 KB segment of the tile
+// One tile's copies: `copies` 1 KB wave copies of 8 rows x 128 bytes each.
+__device__ __forceinline__ void copy_rows(int8_t *dst, const int8_t *src, int copies, int nwaves,
+                                          uint32_t rows_limit, uint32_t r0, uint32_t K, uint32_t kb,
+                                          int wave, int lane) {
+    for (int i = 0; i < copies; ++i) {
+        const int seg = i * nwaves + wave;  // 1 KB segment of the tile
         const uint32_t row = seg * kRowsPerCopy + lane / kChunksPerRow;
         const uint32_t chunk = (lane % kChunksPerRow) ^ chunk_swz(row);
         const uint64_t kof = min((uint64_t)kb * 32 + chunk * 16, (uint64_t)K - 16);
-        __builtin_amdgcn_global_load_lds(a + (uint64_t)min(m0 + row, M - 1) * K + kof,
-                                         (lds_void *)(st.a + seg * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(w + (uint64_t)min(n0 + row, N - 1) * K + kof,
-                                         (lds_void *)(st.w + seg * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src + (uint64_t)min(r0 + row, rows_limit - 1) * K + kof,
+                                         (lds_void *)(dst + seg * 1024), 16, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < kScaleCopiesPerWave; ++i) {
-        const int seg = i * kWaves + wave;                       // 64 floats of the scale tile
-        const uint32_t idx = seg * 64 + lane;                    // = row * kGemmStageBlocks + block
+}
+
+// One scale tile's copies: `copies` 64-float wave copies, consecutive lanes on
+// consecutive blocks of a row.
+__device__ __forceinline__ void copy_scales(float *dst, const float *src, int copies, int nwaves,
+                                            uint32_t rows_limit, uint32_t r0, uint32_t nb, uint32_t kb,
+                                            int wave, int lane) {
+    for (int i = 0; i < copies; ++i) {
+        const int seg = i * nwaves + wave;
+        const uint32_t idx = seg * 64 + lane;  // = row * kGemmStageBlocks + block
         const uint32_t row = idx / kGemmStageBlocks;
         const uint32_t blk = min(kb + idx % kGemmStageBlocks, nb - 1);
-        __builtin_amdgcn_global_load_lds(a_s + (uint64_t)min(m0 + row, M - 1) * nb + blk,
-                                         (lds_void *)(&st.as[0][0] + seg * 64), 4, 0, 0);
-        __builtin_amdgcn_global_load_lds(w_s + (uint64_t)min(n0 + row, N - 1) * nb + blk,
-                                         (lds_void *)(&st.ws[0][0] + seg * 64), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(src + (uint64_t)min(r0 + row, rows_limit - 1) * nb + blk,
+                                         (lds_void *)(dst + seg * 64), 4, 0, 0);
+    }
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void issue_stage(Stage<BM, BN> &st, const int8_t *a, const int8_t *w,
+                                            const float *a_s, const float *w_s, uint32_t M,
+                                            uint32_t N, uint32_t K, uint32_t nb, uint32_t m0,
+                                            uint32_t n0, uint32_t kb, int wave, int lane) {
+    using G = Geo<BM, BN>;
+#pragma unroll
+    for (int i = 0; i < 1; ++i) {
+        copy_rows(st.a, a, G::kACopies, G::kWaves, M, m0, K, kb, wave, lane);
+        copy_rows(st.w, w, G::kWCopies, G::kWaves, N, n0, K, kb, wave, lane);
+        copy_scales(&st.as[0][0], a_s, G::kASCopies, G::kWaves, M, m0, nb, kb, wave, lane);
+        copy_scales(&st.ws[0][0], w_s, G::kWSCopies, G::kWaves, N, n0, nb, kb, wave, lane);
     }
 }
 
@@ -131,19 +159,23 @@ __device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "
                  "+v"(x[6]), "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]),    \
                  "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15]))
 
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(
+template <int BM, int BN>
+__global__ __launch_bounds__(BM * BN / 64, 32768 / (BM * BN)) void gemm_kernel(
     const int8_t *__restrict__ a, const int8_t *__restrict__ w, const float *__restrict__ a_s,
     const float *__restrict__ w_s, uint16_t *__restrict__ out, uint32_t M, uint32_t N, uint32_t K,
     uint32_t tiles_m, uint32_t tiles_n) {
-    __shared__ __attribute__((aligned(1024))) Stage ring[kGemmRing];
+    using G = Geo<BM, BN>;
+    static_assert(G::kThreads == BM * BN / 64, "launch bound matches the wave count");
+    using St = Stage<BM, BN>;
+    __shared__ __attribute__((aligned(1024))) St ring[kGemmRing];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / G::kWavesN, wn = wave % G::kWavesN;
     uint32_t tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-    const uint32_t m0 = tm * kGemmBM, n0 = tn * kGemmBN;
+    const uint32_t m0 = tm * BM, n0 = tn * BN;
     const uint32_t nb = K / 32;
     const uint32_t nstages = (nb + kGemmStageBlocks - 1) / kGemmStageBlocks;
 
@@ -177,7 +209,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(
     // block j).  The matrix-core result of unit u + 1 (and the scale products of
     // its tile) is requested before unit u is rescaled, so each rescale reads a
     // result that finished while the previous unit's 32 VALU instructions ran.
-    auto pair = [&](const Stage &cur, uint32_t kb, int jp) {
+    auto pair = [&](const St &cur, uint32_t kb, int jp) {
         v4i af[2][2], bf[2][2];
         float asv[2], wsv[2];
         // lanes 0-31 carry block jp, lanes 32-63 block jp + 1 (zero if past K)
@@ -213,7 +245,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(
                 ac[r] = fmaf((float)p[u & 1][r], sc[t & 1][16 * j + r], ac[r]);
         }
     };
-    auto compute = [&](const Stage &cur, uint32_t kb) {
+    auto compute = [&](const St &cur, uint32_t kb) {
 #pragma unroll
         for (int jp = 0; jp < kGemmStageBlocks; jp += 2) {
             pair(cur, kb, jp);
@@ -225,14 +257,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(
         BSR_PIN16(acc[1][0]);
         BSR_PIN16(acc[1][1]);
     };
-    auto issue = [&](Stage &buf, uint32_t stage) {
-        issue_stage(buf, a, w, a_s, w_s, M, N, K, nb, m0, n0, stage * kGemmStageBlocks, wave, lane);
+    auto issue = [&](St &buf, uint32_t stage) {
+        issue_stage<BM, BN>(buf, a, w, a_s, w_s, M, N, K, nb, m0, n0, stage * kGemmStageBlocks, wave, lane);
     };
     // Stage s lives in buffer s % 2.  At the top of stage s each wave waits for
     // its own copies of stage s, the barrier publishes every wave's copies and
     // frees the other buffer (its stage s - 1 reads are done), and the copies of
     // stage s + 1 go out before stage s is computed.
-    auto step = [&](Stage &cur, Stage &next, uint32_t s) {
+    auto step = [&](St &cur, St &next, uint32_t s) {
         wait_copies<0>();
         stage_barrier();
         if (s + 1 < nstages) issue(next, s + 1);
@@ -260,16 +292,25 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(
         }
 }
 
+template <int BM, int BN>
+hipError_t launch_tiles(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
+                        const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                        hipStream_t s) {
+    const uint32_t tiles_m = (uint32_t)div_up(m, BM);
+    const uint32_t tiles_n = (uint32_t)div_up(n, BN);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN>), dim3(tiles_m * tiles_n), dim3(Geo<BM, BN>::kThreads), 0, s,
+                       a_i8, w_i8, a_scale, w_scale, out, m, n, k, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
                        const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                        hipStream_t s) {
-    const uint32_t tiles_m = (uint32_t)div_up(m, kGemmBM);
-    const uint32_t tiles_n = (uint32_t)div_up(n, kGemmBN);
-    hipLaunchKernelGGL(gemm_kernel, dim3(tiles_m * tiles_n), dim3(kGemmThreads), 0, s, a_i8, w_i8,
-                       a_scale, w_scale, out, m, n, k, tiles_m, tiles_n);
-    return hipGetLastError();
+    if (m <= (uint32_t)kGemmBMSmall)
+        return launch_tiles<kGemmBMSmall, kGemmBN>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, s);
+    return launch_tiles<kGemmBMLarge, kGemmBN>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, s);
 }
 
 }  // namespace bsr
