@@ -41,7 +41,8 @@ def _args():
     p.add_argument("--decode-iters", type=int, default=100)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
-    p.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    p.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
+                   help="copy: a plain 256 MiB device copy, the known-size reference for HBM byte counters")
     return p.parse_args()
 
 
@@ -83,6 +84,17 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     rec = {}
+
+    if args.only == "copy":
+        # known-size reference for rocprofv3 FETCH_SIZE / WRITE_SIZE: each copy
+        # reads and writes exactly 256 MiB
+        src = torch.ones(256 * 2 ** 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel(), "copies": 5}), flush=True)
+        return
 
     def dev_t(x):
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
