@@ -18,13 +18,14 @@ constexpr int kRqaLanesPerBlock = 4;
 constexpr int kRqwThreads = 256;
 
 // ---- GEMM (m > 8) ---------------------------------------------------------
-// A workgroup computes a BM x BN output tile with (BM/64) x (BN/64) waves, each
-// owning a 64 x 64 piece as 2 x 2 MFMA 32x32 tiles.  The K loop stages
-// kGemmStageBlocks 32-wide blocks of A, W and their scales per LDS buffer, in
-// a ring of kGemmRing buffers.  Workgroups are ordered so that each XCD runs a
-// compact kGemmGroupM-tall group of output tiles.  Two tile shapes are built:
-// 256 x 128 (8 waves, the default) and 128 x 128 (4 waves, for m <= 128).
-constexpr int kGemmWaveTile = 64;
+// A workgroup computes a BM x BN output tile; each wave owns a WM x WN piece
+// made of 32 x 32 MFMA tiles.  The K loop stages kGemmStageBlocks 32-wide
+// blocks of A, W and their scales per LDS buffer, in a ring of kGemmRing
+// buffers.  Workgroups are ordered so that each XCD runs a compact
+// kGemmGroupM-tall group of output tiles.  Three shapes are built: 128 x 128
+// with sixteen 32 x 32 waves (m <= 128), 256 x 128 with eight 64 x 64 waves
+// (grids of up to two rounds over the CUs), and 128 x 128 with four 64 x 64
+// waves and two workgroups per CU (larger grids).
 constexpr int kGemmBMLarge = 256;
 constexpr int kGemmBMSmall = 128;
 constexpr int kGemmBN = 128;
@@ -33,6 +34,7 @@ constexpr int kGemmStageBytes = 32 * kGemmStageBlocks;    // 128 bytes of K per 
 constexpr int kGemmRing = 2;                              // stage buffers in flight
 constexpr int kGemmGroupM = 8;
 constexpr int kXcds = 8;
+constexpr int kGemmCus = 256;                             // compute units of an MI355X
 
 // ---- GEMV (m <= 8) --------------------------------------------------------
 // A workgroup owns kGemvCols output columns and splits K over its waves; each

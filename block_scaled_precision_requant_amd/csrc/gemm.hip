@@ -34,20 +34,15 @@ static_assert(kGemmStageBlocks % 2 == 0, "the 2-block f32 MFMA covers pairs of b
 static_assert(kGemmRing == 2, "the loop below alternates two buffers");
 
 // Geometry of one tile shape.
-template <int BM, int BN>
+template <int BM, int BN, int WM, int WN>
 struct Geo {
-    static constexpr int kWavesM = BM / kGemmWaveTile, kWavesN = BN / kGemmWaveTile;
+    static constexpr int kTM = WM / 32, kTN = WN / 32;  // 32x32 MFMA tiles per wave
+    static constexpr int kWavesM = BM / WM, kWavesN = BN / WN;
     static constexpr int kWaves = kWavesM * kWavesN;
     static constexpr int kThreads = 64 * kWaves;
-    static constexpr int kACopies = BM / (kRowsPerCopy * kWaves);            // 1 KB copies per wave
-    static constexpr int kWCopies = BN / (kRowsPerCopy * kWaves);
-    static constexpr int kASCopies = BM * kGemmStageBlocks / (64 * kWaves);  // 64-float copies per wave
-    static constexpr int kWSCopies = BN * kGemmStageBlocks / (64 * kWaves);
-    static_assert(kACopies * kRowsPerCopy * kWaves == BM && kWCopies * kRowsPerCopy * kWaves == BN,
-                  "tile rows split evenly over the waves' copies");
-    static_assert(kASCopies * 64 * kWaves == BM * kGemmStageBlocks &&
-                      kWSCopies * 64 * kWaves == BN * kGemmStageBlocks,
-                  "scale tiles split evenly over the waves' copies");
+    static_assert(BM % (kRowsPerCopy) == 0 && BN % kRowsPerCopy == 0, "whole 1 KB copy segments");
+    static_assert((BM * kGemmStageBlocks) % 64 == 0 && (BN * kGemmStageBlocks) % 64 == 0,
+                  "whole 64-float scale segments");
 };
 
 // Workgroup -> output tile.  Workgroups are dispatched round-robin over the
@@ -74,11 +69,17 @@ __device__ __forceinline__ void tile_of(uint32_t wg, uint32_t tiles_m, uint32_t 
 // pairs, so a 64-lane ds_read_b128 is conflict-free on 32- or 64-bank LDS.
 __device__ __forceinline__ uint32_t chunk_swz(uint32_t r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+// Scale tiles are [row][block] with the 4 blocks of row r permuted by
+// scale_swz(r): 32 consecutive rows read at one block then fall in 32 distinct
+// banks (32- or 64-bank LDS), instead of 4 rows per bank.
+__device__ __forceinline__ uint32_t scale_swz(uint32_t r) { return (r >> 3) & 3; }
+static_assert(kGemmStageBlocks == 4, "scale_swz permutes 4 blocks");
+
 template <int BM, int BN>
 struct Stage {
     int8_t a[BM * kGemmStageBytes];
     int8_t w[BN * kGemmStageBytes];
-    float as[BM][kGemmStageBlocks];  // [row][block of the stage]
+    float as[BM][kGemmStageBlocks];  // [row][block ^ scale_swz(row)]
     float ws[BN][kGemmStageBlocks];
 };
 
@@ -89,12 +90,15 @@ struct Stage {
 // re-read the last one, and the compute zeroes the scale product of any block
 // past K.  Scale copies map consecutive lanes to consecutive blocks of a row,
 // so one copy touches 16 rows' worth of contiguous bytes.
-// One tile's copies: `copies` 1 KB wave copies of 8 rows x 128 bytes each.
-__device__ __forceinline__ void copy_rows(int8_t *dst, const int8_t *src, int copies, int nwaves,
-                                          uint32_t rows_limit, uint32_t r0, uint32_t K, uint32_t kb,
-                                          int wave, int lane) {
-    for (int i = 0; i < copies; ++i) {
-        const int seg = i * nwaves + wave;  // 1 KB segment of the tile
+// One tile's copies: NSEGS 1 KB segments of 8 rows x 128 bytes, segment `seg`
+// issued by wave seg % NWAVES (compile-time trip counts, fully unrolled).
+template <int NSEGS, int NWAVES>
+__device__ __forceinline__ void copy_rows(int8_t *dst, const int8_t *src, uint32_t rows_limit,
+                                          uint32_t r0, uint32_t K, uint32_t kb, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < (NSEGS + NWAVES - 1) / NWAVES; ++i) {
+        const int seg = wave + i * NWAVES;
+        if (NSEGS % NWAVES != 0 && seg >= NSEGS) break;
         const uint32_t row = seg * kRowsPerCopy + lane / kChunksPerRow;
         const uint32_t chunk = (lane % kChunksPerRow) ^ chunk_swz(row);
         const uint64_t kof = min((uint64_t)kb * 32 + chunk * 16, (uint64_t)K - 16);
@@ -103,34 +107,32 @@ __device__ __forceinline__ void copy_rows(int8_t *dst, const int8_t *src, int co
     }
 }
 
-// One scale tile's copies: `copies` 64-float wave copies, consecutive lanes on
-// consecutive blocks of a row.
-__device__ __forceinline__ void copy_scales(float *dst, const float *src, int copies, int nwaves,
-                                            uint32_t rows_limit, uint32_t r0, uint32_t nb, uint32_t kb,
-                                            int wave, int lane) {
-    for (int i = 0; i < copies; ++i) {
-        const int seg = i * nwaves + wave;
-        const uint32_t idx = seg * 64 + lane;  // = row * kGemmStageBlocks + block
+// One scale tile's copies: NSEGS segments of 64 floats, consecutive lanes on
+// the (swizzled) blocks of a row.
+template <int NSEGS, int NWAVES>
+__device__ __forceinline__ void copy_scales(float *dst, const float *src, uint32_t rows_limit,
+                                            uint32_t r0, uint32_t nb, uint32_t kb, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < (NSEGS + NWAVES - 1) / NWAVES; ++i) {
+        const int seg = wave + i * NWAVES;
+        if (NSEGS % NWAVES != 0 && seg >= NSEGS) break;
+        const uint32_t idx = seg * 64 + lane;  // = row * kGemmStageBlocks + slot
         const uint32_t row = idx / kGemmStageBlocks;
-        const uint32_t blk = min(kb + idx % kGemmStageBlocks, nb - 1);
+        const uint32_t blk = min(kb + ((idx % kGemmStageBlocks) ^ scale_swz(row)), nb - 1);
         __builtin_amdgcn_global_load_lds(src + (uint64_t)min(r0 + row, rows_limit - 1) * nb + blk,
                                          (lds_void *)(dst + seg * 64), 4, 0, 0);
     }
 }
 
-template <int BM, int BN>
+template <class G, int BM, int BN>
 __device__ __forceinline__ void issue_stage(Stage<BM, BN> &st, const int8_t *a, const int8_t *w,
                                             const float *a_s, const float *w_s, uint32_t M,
                                             uint32_t N, uint32_t K, uint32_t nb, uint32_t m0,
                                             uint32_t n0, uint32_t kb, int wave, int lane) {
-    using G = Geo<BM, BN>;
-#pragma unroll
-    for (int i = 0; i < 1; ++i) {
-        copy_rows(st.a, a, G::kACopies, G::kWaves, M, m0, K, kb, wave, lane);
-        copy_rows(st.w, w, G::kWCopies, G::kWaves, N, n0, K, kb, wave, lane);
-        copy_scales(&st.as[0][0], a_s, G::kASCopies, G::kWaves, M, m0, nb, kb, wave, lane);
-        copy_scales(&st.ws[0][0], w_s, G::kWSCopies, G::kWaves, N, n0, nb, kb, wave, lane);
-    }
+    copy_rows<BM / kRowsPerCopy, G::kWaves>(st.a, a, M, m0, K, kb, wave, lane);
+    copy_rows<BN / kRowsPerCopy, G::kWaves>(st.w, w, N, n0, K, kb, wave, lane);
+    copy_scales<BM * kGemmStageBlocks / 64, G::kWaves>(&st.as[0][0], a_s, M, m0, nb, kb, wave, lane);
+    copy_scales<BN * kGemmStageBlocks / 64, G::kWaves>(&st.ws[0][0], w_s, N, n0, nb, kb, wave, lane);
 }
 
 // Wait until at most n of this wave's global -> LDS copies are outstanding.
@@ -159,19 +161,19 @@ __device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "
                  "+v"(x[6]), "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]),    \
                  "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15]))
 
-template <int BM, int BN>
-__global__ __launch_bounds__(BM * BN / 64, 32768 / (BM * BN)) void gemm_kernel(
+template <int BM, int BN, int WM, int WN, int WG_PER_CU>
+__global__ __launch_bounds__(BM * BN / (WM * WN) * 64, WG_PER_CU) void gemm_kernel(
     const int8_t *__restrict__ a, const int8_t *__restrict__ w, const float *__restrict__ a_s,
     const float *__restrict__ w_s, uint16_t *__restrict__ out, uint32_t M, uint32_t N, uint32_t K,
     uint32_t tiles_m, uint32_t tiles_n) {
-    using G = Geo<BM, BN>;
-    static_assert(G::kThreads == BM * BN / 64, "launch bound matches the wave count");
+    using G = Geo<BM, BN, WM, WN>;
+    constexpr int TM = G::kTM, TN = G::kTN;
     using St = Stage<BM, BN>;
     __shared__ __attribute__((aligned(1024))) St ring[kGemmRing];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / G::kWavesN, wn = wave % G::kWavesN;
     uint32_t tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -184,65 +186,72 @@ __global__ __launch_bounds__(BM * BN / 64, 32768 / (BM * BN)) void gemm_kernel(
     // half (l / 32) of it.
     const uint32_t sw = chunk_swz(lane & 31);
     const int half = lane >> 5;
-    int off_a[2][kGemmStageBlocks], off_w[2][kGemmStageBlocks];
+    // (rows of a tile differ by 32 * 128 bytes, a constant the compiler folds
+    // into the ds_read offset, so one offset per block is kept)
+    int off_a[kGemmStageBlocks], off_w[kGemmStageBlocks];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int j = 0; j < kGemmStageBlocks; ++j) {
-            const int chunk = 2 * j + half;
-            off_a[t][j] = (wm * 64 + t * 32 + (lane & 31)) * kGemmStageBytes + ((chunk ^ sw) << 4);
-            off_w[t][j] = (wn * 64 + t * 32 + (lane & 31)) * kGemmStageBytes + ((chunk ^ sw) << 4);
-        }
+    for (int j = 0; j < kGemmStageBlocks; ++j) {
+        const int chunk = 2 * j + half;
+        off_a[j] = (wm * WM + (lane & 31)) * kGemmStageBytes + ((chunk ^ sw) << 4);
+        off_w[j] = (wn * WN + (lane & 31)) * kGemmStageBytes + ((chunk ^ sw) << 4);
+    }
 
-    float acc[2][2][16];
+    float acc[TM][TN][16];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const v16i zero16 = {};
     const v32f zero32 = {};
 
-    // A block pair (blocks jp, jp + 1 of the stage) = 8 units (tile t = 2 sm + sn,
-    // block j).  The matrix-core result of unit u + 1 (and the scale products of
-    // its tile) is requested before unit u is rescaled, so each rescale reads a
-    // result that finished while the previous unit's 32 VALU instructions ran.
+    // A block pair (blocks jp, jp + 1 of the stage) = 2 * TM * TN units (tile
+    // t = sm * TN + sn, block j).  The matrix-core result of unit u + 1 (and the
+    // scale products of its tile) is requested before unit u is rescaled, so
+    // each rescale reads a result that finished while the previous unit's 32
+    // VALU instructions ran.
     auto pair = [&](const St &cur, uint32_t kb, int jp) {
-        v4i af[2][2], bf[2][2];
-        float asv[2], wsv[2];
+        v4i af[TM][2], bf[TN][2];
+        float asv[TM], wsv[TN];
         // lanes 0-31 carry block jp, lanes 32-63 block jp + 1 (zero if past K)
         const bool blk_live = kb + jp + half < nb;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < TM; ++t) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                af[t][j] = *reinterpret_cast<const v4i *>(cur.a + off_a[t][jp + j]);
-                bf[t][j] = *reinterpret_cast<const v4i *>(cur.w + off_w[t][jp + j]);
-            }
-            const float av = cur.as[wm * 64 + t * 32 + (lane & 31)][jp + half];
+            for (int j = 0; j < 2; ++j)
+                af[t][j] = *reinterpret_cast<const v4i *>(cur.a + off_a[jp + j] + t * 32 * kGemmStageBytes);
+            const uint32_t ra = wm * WM + t * 32 + (lane & 31);
+            const float av = cur.as[ra][(jp + half) ^ scale_swz(ra)];
             asv[t] = blk_live ? av : 0.0f;
-            wsv[t] = cur.ws[wn * 64 + t * 32 + (lane & 31)][jp + half];
         }
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bf[t][j] = *reinterpret_cast<const v4i *>(cur.w + off_w[jp + j] + t * 32 * kGemmStageBytes);
+            const uint32_t rw = wn * WN + t * 32 + (lane & 31);
+            wsv[t] = cur.ws[rw][(jp + half) ^ scale_swz(rw)];
+        }
+        constexpr int kUnits = 2 * TM * TN;
         v32f sc[2];
         v16i p[2];
         sc[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(asv[0], wsv[0], zero32, 0, 0, 0);
         p[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[0][0], bf[0][0], zero16, 0, 0, 0);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < kUnits; ++u) {
             const int t = u >> 1, j = u & 1;
-            if (u + 1 < 8) {
+            if (u + 1 < kUnits) {
                 const int t1 = (u + 1) >> 1, j1 = (u + 1) & 1;
                 if (j1 == 0)
-                    sc[t1 & 1] = __builtin_amdgcn_mfma_f32_32x32x1f32(asv[t1 >> 1], wsv[t1 & 1], zero32, 0, 0, 0);
+                    sc[t1 & 1] = __builtin_amdgcn_mfma_f32_32x32x1f32(asv[t1 / TN], wsv[t1 % TN], zero32, 0, 0, 0);
                 p[(u + 1) & 1] =
-                    __builtin_amdgcn_mfma_i32_32x32x32_i8(af[t1 >> 1][j1], bf[t1 & 1][j1], zero16, 0, 0, 0);
+                    __builtin_amdgcn_mfma_i32_32x32x32_i8(af[t1 / TN][j1], bf[t1 % TN][j1], zero16, 0, 0, 0);
             }
-            float *ac = acc[t >> 1][t & 1];
+            float *ac = acc[t / TN][t % TN];
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                ac[r] = fmaf((float)p[u & 1][r], sc[t & 1][16 * j + r], ac[r]);
+            for (int r = 0; r < 16; ++r) ac[r] = fmaf((float)p[u & 1][r], sc[t & 1][16 * j + r], ac[r]);
         }
     };
     auto compute = [&](const St &cur, uint32_t kb) {
@@ -252,13 +261,13 @@ __global__ __launch_bounds__(BM * BN / 64, 32768 / (BM * BN)) void gemm_kernel(
             // read the next pair's operands only after this pair: bounds live registers
             asm volatile("" ::: "memory");
         }
-        BSR_PIN16(acc[0][0]);
-        BSR_PIN16(acc[0][1]);
-        BSR_PIN16(acc[1][0]);
-        BSR_PIN16(acc[1][1]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) BSR_PIN16(acc[i][j]);
     };
     auto issue = [&](St &buf, uint32_t stage) {
-        issue_stage<BM, BN>(buf, a, w, a_s, w_s, M, N, K, nb, m0, n0, stage * kGemmStageBlocks, wave, lane);
+        issue_stage<G>(buf, a, w, a_s, w_s, M, N, K, nb, m0, n0, stage * kGemmStageBlocks, wave, lane);
     };
     // Stage s lives in buffer s % 2.  At the top of stage s each wave waits for
     // its own copies of stage s, the barrier publishes every wave's copies and
@@ -280,26 +289,27 @@ __global__ __launch_bounds__(BM * BN / 64, 32768 / (BM * BN)) void gemm_kernel(
     // Output layout of a 32x32 MFMA tile: lane l holds column l % 32 and, in
     // register r, row 8 * (r / 4) + 4 * (l / 32) + r % 4.
 #pragma unroll
-    for (int sm = 0; sm < 2; ++sm)
+    for (int sm = 0; sm < TM; ++sm)
 #pragma unroll
-        for (int sn = 0; sn < 2; ++sn) {
-            const uint32_t col = n0 + wn * 64 + sn * 32 + (lane & 31);
+        for (int sn = 0; sn < TN; ++sn) {
+            const uint32_t col = n0 + wn * WN + sn * 32 + (lane & 31);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const uint32_t row = m0 + wm * 64 + sm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const uint32_t row = m0 + wm * WM + sm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 if (row < M && col < N) out[(uint64_t)row * N + col] = f32_to_bf16_rne(acc[sm][sn][r]);
             }
         }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WM, int WN, int WG_PER_CU>
 hipError_t launch_tiles(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
                         const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                         hipStream_t s) {
     const uint32_t tiles_m = (uint32_t)div_up(m, BM);
     const uint32_t tiles_n = (uint32_t)div_up(n, BN);
-    hipLaunchKernelGGL((gemm_kernel<BM, BN>), dim3(tiles_m * tiles_n), dim3(Geo<BM, BN>::kThreads), 0, s,
-                       a_i8, w_i8, a_scale, w_scale, out, m, n, k, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, WG_PER_CU>), dim3(tiles_m * tiles_n),
+                       dim3(Geo<BM, BN, WM, WN>::kThreads), 0, s, a_i8, w_i8, a_scale, w_scale, out, m, n,
+                       k, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
@@ -308,9 +318,17 @@ hipError_t launch_tiles(const int8_t *a_i8, const int8_t *w_i8, const float *a_s
 hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
                        const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                        hipStream_t s) {
+    // m <= 128: one tile row; sixteen 32x32 waves per 128x128 tile keep four
+    // waves on every SIMD although the grid is small.
     if (m <= (uint32_t)kGemmBMSmall)
-        return launch_tiles<kGemmBMSmall, kGemmBN>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, s);
-    return launch_tiles<kGemmBMLarge, kGemmBN>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, s);
+        return launch_tiles<kGemmBMSmall, kGemmBN, 32, 32, 1>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, s);
+    // Up to two rounds of 256x128 tiles over the CUs: one 8-wave workgroup per
+    // CU.  Larger grids: two 4-wave 128x128 workgroups per CU, whose barriers
+    // fall at different times, so one computes while the other waits.
+    const uint64_t big_tiles = div_up(m, kGemmBMLarge) * div_up(n, kGemmBN);
+    if (big_tiles <= 2 * (uint64_t)kGemmCus)
+        return launch_tiles<kGemmBMLarge, kGemmBN, 64, 64, 1>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, s);
+    return launch_tiles<kGemmBMSmall, kGemmBN, 64, 64, 2>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, s);
 }
 
 }  // namespace bsr
