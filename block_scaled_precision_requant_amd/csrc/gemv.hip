@@ -10,12 +10,21 @@
 // split K into contiguous ranges.  A wave step covers 64 bytes of K (two scale
 // blocks) for its 16 columns: lane l loads 16 bytes of weight row (n0 + l % 16)
 // at byte 16 * (l / 16) of the step -- 16 rows x 64 contiguous bytes per
-// instruction -- and, if l % 16 < m, 16 bytes of activation row l % 16 at the
-// same offset.  One v_mfma_i32_16x16x64_i8 with the activation quarters 2-3
-// zeroed gives the first block's P, one with quarters 0-1 zeroed the second's:
-// lanes pair A and B bytes by (quarter, byte), so the zeroed quarters drop out
+// instruction -- and takes 16 bytes of activation row l % 16 (clamped to the
+// last row; rows >= m only feed outputs that are never stored) at the same
+// offset.  One v_mfma_i32_16x16x64_i8 with the activation quarters 2-3 zeroed
+// gives the first block's P, one with quarters 0-1 zeroed the second's: lanes
+// pair A and B bytes by (quarter, byte), so the zeroed quarters drop out
 // exactly.  Output lane l holds column l % 16, rows 4 * (l / 16) + r (r < 4),
 // so lanes 0-31 hold all m <= 8 rows.
+//
+// Two kernels share that arithmetic:
+//  * staged: the workgroup first copies its activations, activation scales
+//    and the scales of its 16 weight rows into LDS (global_load_lds), so the
+//    only global loads of the K loop are weight bytes -- one 1 KB instruction
+//    per wave step;
+//  * direct: every operand comes from global memory.  Used when the staged
+//    copies do not fit in LDS or K is not a multiple of 128.
 #include "bsr_internal.h"
 
 namespace bsr {
@@ -23,6 +32,72 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kSteps = kGemvBlocksPerIter / 2;  // 64-byte MFMA steps per iteration
+constexpr int kQuads = kGemvBlocksPerIter / 4;  // groups of 4 scales per iteration
+static_assert(kGemvBlocksPerIter % 4 == 0, "scales are read 4 blocks at a time");
+
+// Operands of one iteration (kGemvBlocksPerIter blocks) of one lane.
+struct IterOps {
+    v4i wv[kSteps], av[kSteps];
+    v4f wsv[kQuads], asv[kQuads][4];  // asv[h][r]: activation row 4q + r
+};
+
+// Rescale-accumulate one iteration.  Blocks at or past b_end (and rows >= m)
+// get zero activations, so their P is 0 and they add nothing.
+__device__ __forceinline__ void gemv_iter(float (&acc)[4], const IterOps &x, uint32_t b0,
+                                          uint32_t b_end, bool a_live, int q) {
+    const v4i zero4 = {0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < kSteps; ++t) {
+        const uint32_t blk = b0 + 2 * t + (q >> 1);  // block of this lane's quarter
+        const bool live = a_live && blk < b_end;
+        const v4i avl = live ? x.av[t] : zero4;
+        const v4i lo = q < 2 ? avl : zero4;  // first block of the step
+        const v4i hi = q < 2 ? zero4 : avl;  // second block
+        const v4i p0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(lo, x.wv[t], zero4, 0, 0, 0);
+        const v4i p1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(hi, x.wv[t], zero4, 0, 0, 0);
+        const int h = t >> 1, e = 2 * (t & 1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            acc[r] = fmaf((float)p0[r], x.asv[h][r][e] * x.wsv[h][e], acc[r]);
+            acc[r] = fmaf((float)p1[r], x.asv[h][r][e + 1] * x.wsv[h][e + 1], acc[r]);
+        }
+    }
+}
+
+// Add the waves' partial sums in wave order and store the live outputs.
+// `red` holds kGemvMaxWaves x 64 x 4 floats; the caller has made it free.
+__device__ __forceinline__ void gemv_reduce_store(float *red, const float (&acc)[4], int wave,
+                                                  int nwaves, int lane, uint32_t n0, uint32_t m,
+                                                  uint32_t n, uint16_t *out) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[(wave * 64 + lane) * 4 + r] = acc[r];
+    __syncthreads();
+    if (wave == 0 && lane < 32) {
+        float tot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int v = 0; v < nwaves; ++v)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tot[r] += red[(v * 64 + lane) * 4 + r];
+        const uint32_t c = n0 + (lane & 15);
+        const int q = lane >> 4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t row = 4 * q + r;
+            if (row < m && c < n) out[(uint64_t)row * n + c] = f32_to_bf16_rne(tot[r]);
+        }
+    }
+}
+
+// s_waitcnt vmcnt(n); expcnt and lgkmcnt left at their maxima.
+template <int n>
+__device__ __forceinline__ void wait_vm_le() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+}
+
+// ---------------------------------------------------------------- direct
 
 // Scales of blocks idx..idx+3 of one row: one 16-byte load when every row
 // holds a multiple of 4 blocks (then idx, a multiple of 4, is 16-byte aligned
@@ -35,14 +110,12 @@ __device__ __forceinline__ v4f load_f4(const float *p, uint32_t idx, uint32_t nb
     return r;
 }
 
-__device__ __forceinline__ float f4(const v4f &v, int i) { return v[i]; }
-
 template <bool VEC>
-__global__ __launch_bounds__(kGemvMaxWaves * 64) void gemv_kernel(
+__global__ __launch_bounds__(kGemvMaxWaves * 64) void gemv_direct_kernel(
     const int8_t *__restrict__ a, const int8_t *__restrict__ w, const float *__restrict__ a_s,
     const float *__restrict__ w_s, uint16_t *__restrict__ out, uint32_t m, uint32_t n, uint32_t k,
     uint32_t blocks_per_wave) {
-    __shared__ float red[kGemvMaxWaves][64][4];
+    __shared__ float red[kGemvMaxWaves * 64 * 4];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -53,8 +126,7 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void gemv_kernel(
     const uint32_t arow = lane & 15;              // activation row this lane feeds
     const bool a_live = arow < m;
     const uint32_t nb = k / 32;
-    // scale rows this lane's outputs need: 4q + r (only q < 2 carries real rows)
-    const uint32_t srow0 = min(4u * (uint32_t)q, m - 1);
+    const uint32_t srow0 = min(4u * (uint32_t)q, m - 1);  // scale rows 4q + r
 
     const int8_t *wrow = w + (uint64_t)col * k;
     const int8_t *arowp = a + (uint64_t)min(arow, m - 1) * k;
@@ -63,65 +135,154 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void gemv_kernel(
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     const uint32_t b_begin = wave * blocks_per_wave;
     const uint32_t b_end = min(nb, b_begin + blocks_per_wave);
-    const v4i zero4 = {0, 0, 0, 0};
-
-    // One iteration = kGemvBlocksPerIter blocks = kSteps 64-byte steps.  Every
-    // load of the iteration is issued before any is used, so each wave keeps
-    // kSteps * 1 KB of weight bytes in flight.
-    constexpr int kSteps = kGemvBlocksPerIter / 2;
-    constexpr int kQuads = kGemvBlocksPerIter / 4;
+    // Every load of an iteration is issued before any is used.
     for (uint32_t b0 = b_begin; b0 < b_end; b0 += kGemvBlocksPerIter) {
-        v4i wv[kSteps], av[kSteps];
-        bool live[kSteps];
+        IterOps x;
 #pragma unroll
         for (int t = 0; t < kSteps; ++t) {
-            const uint32_t blk = b0 + 2 * t + (q >> 1);  // block of this lane's quarter
             const uint64_t off = min((uint64_t)b0 * 32 + 64 * t + 16 * q, (uint64_t)k - 16);
-            wv[t] = *reinterpret_cast<const v4i *>(wrow + off);
-            av[t] = *reinterpret_cast<const v4i *>(arowp + off);  // dead lanes zeroed below
-            live[t] = a_live && blk < b_end;
+            x.wv[t] = *reinterpret_cast<const v4i *>(wrow + off);
+            x.av[t] = *reinterpret_cast<const v4i *>(arowp + off);
         }
-        v4f wsv[kQuads], asv[kQuads][4];
 #pragma unroll
         for (int h = 0; h < kQuads; ++h) {
-            wsv[h] = load_f4<VEC>(wsrow, b0 + 4 * h, nb);
+            x.wsv[h] = load_f4<VEC>(wsrow, b0 + 4 * h, nb);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                asv[h][r] = load_f4<VEC>(a_s + (uint64_t)min(srow0 + r, m - 1) * nb, b0 + 4 * h, nb);
+                x.asv[h][r] = load_f4<VEC>(a_s + (uint64_t)min(srow0 + r, m - 1) * nb, b0 + 4 * h, nb);
         }
+        gemv_iter(acc, x, b0, b_end, a_live, q);
+    }
+    gemv_reduce_store(red, acc, wave, nwaves, lane, n0, m, n, out);
+}
+
+// ---------------------------------------------------------------- staged
+
+// Each wave stages the slices of A, a_s and w_s that its own K range needs
+// into a private LDS region, so no barrier precedes the K loop.  Region of a
+// wave (bytes): m activation rows of a_pitch bytes, then m activation-scale
+// rows and kGemvCols weight-scale rows of s_pitch floats.  The 16-byte row
+// padding of a_pitch shifts consecutive rows by 4 banks, so the 16 lanes of a
+// quarter (16 rows, one offset) hit 16 distinct banks; s_pitch is padded by 4
+// floats when bpw / 4 is even, for the same reason on the weight-scale rows.
+struct StagedGeo {
+    uint32_t a_pitch, s_pitch, wave_bytes;
+};
+
+__host__ __device__ inline StagedGeo staged_geo(uint32_t m, uint32_t bpw) {
+    StagedGeo g;
+    g.a_pitch = bpw * 32 + 16;
+    g.s_pitch = ((bpw / 4) & 1) ? bpw : bpw + 4;
+    g.wave_bytes = (m * g.a_pitch + (m + kGemvCols) * g.s_pitch * 4 + 15) / 16 * 16;
+    return g;
+}
+
+constexpr uint32_t kLdsBytes = 160 * 1024;           // LDS of a gfx950 workgroup
+constexpr uint32_t kRedBytes = kGemvMaxWaves * 64 * 4 * 4;
+constexpr int kStagedMaxIters = 8;                   // iterations per wave (unrolled)
+
+// Staged kernel with every iteration of a wave unrolled (at most
+// kStagedMaxIters): straight-line code, so the compiler's vmcnt waits count
+// exactly the weight loads issued after the ones an iteration needs.
+// (The weight pointer is not __restrict__: a restrict-qualified read-only
+// load may be moved across the empty asm statements that order the loads.)
+__global__ __launch_bounds__(kGemvMaxWaves * 64) void gemv_staged_kernel(
+    const int8_t *__restrict__ a, const int8_t *w, const float *__restrict__ a_s,
+    const float *__restrict__ w_s, uint16_t *__restrict__ out, uint32_t m, uint32_t n, uint32_t k,
+    uint32_t bpw) {
+    extern __shared__ __attribute__((aligned(1024))) int8_t smem[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nwaves = blockDim.x >> 6;
+    const int q = lane >> 4;
+    const uint32_t n0 = blockIdx.x * kGemvCols;
+    const uint32_t nb = k / 32;
+    const StagedGeo g = staged_geo(m, bpw);
+    const uint32_t b_begin = wave * bpw;
+    const uint32_t b_end = min(nb, b_begin + bpw);
+    const uint32_t len = b_end - b_begin;          // a multiple of 4, at least 4
+    const uint32_t niter = len / kGemvBlocksPerIter;
+    int8_t *la = smem + (uint64_t)wave * g.wave_bytes;
+    float *ls = reinterpret_cast<float *>(la + m * g.a_pitch);
+
+    const uint32_t col = min(n0 + (lane & 15), n - 1);
+    const uint32_t arow = lane & 15;
+    const bool a_live = arow < m;
+    const int8_t *wrow = w + (uint64_t)col * k + (uint64_t)b_begin * 32 + 16 * q;
+    auto load_w = [&](v4i (&wv)[kSteps], uint32_t it) {
 #pragma unroll
-        for (int t = 0; t < kSteps; ++t) {
-            const v4i avl = live[t] ? av[t] : zero4;
-            const v4i lo = q < 2 ? avl : zero4;  // first block of the step
-            const v4i hi = q < 2 ? zero4 : avl;  // second block
-            const v4i p0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(lo, wv[t], zero4, 0, 0, 0);
-            const v4i p1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(hi, wv[t], zero4, 0, 0, 0);
-            // blocks past b_end have zero activations, so P = 0 and they add nothing
-            const int h = t >> 1, e = 2 * (t & 1);
+        for (int t = 0; t < kSteps; ++t)
+            wv[t] = *reinterpret_cast<const v4i *>(wrow + (uint64_t)it * kGemvBlocksPerIter * 32 + 64 * t);
+    };
+
+    // First iteration's weights, then the staging copies, then one wait for
+    // all of them: the weight bytes arrive during the staging latency.
+    v4i wv0[kSteps], wv1[kSteps];
+    load_w(wv0, 0);
+    asm volatile("" ::: "memory");
+    // A slice: m rows of len * 32 bytes, flattened in 1 KB copies; lanes past
+    // the region are masked, lanes in a row's padding re-read its last chunk.
+    const uint32_t a_bytes = m * g.a_pitch;
+    for (uint32_t p0 = 0; p0 < a_bytes; p0 += 1024) {
+        const uint32_t p = p0 + 16 * lane;
+        const uint32_t r = p / g.a_pitch, c = min(p % g.a_pitch, len * 32 - 16);
+        if (p < a_bytes)
+            __builtin_amdgcn_global_load_lds(a + (uint64_t)min(r, m - 1) * k + (uint64_t)b_begin * 32 + c,
+                                             (lds_void *)(la + p0), 16, 0, 0);
+    }
+    // Scale slices: m rows of a_s then 16 rows of w_s, len floats each, in
+    // 16-byte copies (b_begin and len are multiples of 4 and so is nb).
+    const uint32_t s_floats = (m + kGemvCols) * g.s_pitch;
+    for (uint32_t p0 = 0; p0 < s_floats; p0 += 256) {
+        const uint32_t p = p0 + 4 * lane;
+        const uint32_t r = min(p / g.s_pitch, m + kGemvCols - 1), c = min(p % g.s_pitch, len - 4);
+        const float *src = r < m ? a_s + (uint64_t)r * nb
+                                 : w_s + (uint64_t)min(n0 + (r - m), n - 1) * nb;
+        if (p < s_floats)
+            __builtin_amdgcn_global_load_lds(src + b_begin + c, (lds_void *)(ls + p0), 16, 0, 0);
+    }
+    wait_vm_le<0>();
+
+    const int8_t *la_row = la + min(arow, m - 1) * g.a_pitch + 16 * q;
+    const float *lws_row = ls + (m + (lane & 15)) * g.s_pitch;
+    const float *las_row[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                acc[r] = fmaf((float)p0[r], f4(asv[h][r], e) * f4(wsv[h], e), acc[r]);
-                acc[r] = fmaf((float)p1[r], f4(asv[h][r], e + 1) * f4(wsv[h], e + 1), acc[r]);
-            }
+    for (int r = 0; r < 4; ++r) las_row[r] = ls + min(4u * q + r, m - 1) * g.s_pitch;
+    auto load_lds = [&](IterOps &x, uint32_t it) {
+        const uint32_t c = it * kGemvBlocksPerIter;
+#pragma unroll
+        for (int t = 0; t < kSteps; ++t) x.av[t] = *reinterpret_cast<const v4i *>(la_row + c * 32 + 64 * t);
+#pragma unroll
+        for (int h = 0; h < kQuads; ++h) {
+            x.wsv[h] = *reinterpret_cast<const v4f *>(lws_row + c + 4 * h);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x.asv[h][r] = *reinterpret_cast<const v4f *>(las_row[r] + c + 4 * h);
         }
+    };
+
+    // Iteration it computes with weights loaded one iteration earlier; its own
+    // step issues the next iteration's weight and LDS loads first.  Loads are
+    // clamped to the last iteration rather than skipped, keeping the code
+    // straight-line.
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    IterOps x[2];
+    load_lds(x[0], 0);
+#pragma unroll
+    for (int it = 0; it < kStagedMaxIters; ++it) {
+        const uint32_t nxt = min((uint32_t)it + 1, niter - 1);
+        if (it & 1) load_w(wv0, nxt); else load_w(wv1, nxt);
+        load_lds(x[(it + 1) & 1], nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        IterOps &cur = x[it & 1];
+#pragma unroll
+        for (int t = 0; t < kSteps; ++t) cur.wv[t] = (it & 1) ? wv1[t] : wv0[t];
+        gemv_iter(acc, cur, b_begin + it * kGemvBlocksPerIter, b_end, a_live, q);
+        if ((uint32_t)it + 1 >= niter) break;
     }
 
-    // add the waves' partial sums in wave order
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][lane][r] = acc[r];
-    __syncthreads();
-    if (wave == 0 && lane < 32) {
-        float tot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int v = 0; v < nwaves; ++v)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) tot[r] += red[v][lane][r];
-        const uint32_t c = n0 + (lane & 15);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint32_t row = 4 * q + r;
-            if (row < m && c < n) out[(uint64_t)row * n + c] = f32_to_bf16_rne(tot[r]);
-        }
-    }
+    __syncthreads();  // every wave is done with its staged operands
+    gemv_reduce_store(reinterpret_cast<float *>(smem), acc, wave, nwaves, lane, n0, m, n, out);
 }
 
 }  // namespace
@@ -130,21 +291,33 @@ hipError_t launch_gemv(const int8_t *a_i8, const int8_t *w_i8, const float *a_sc
                        const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                        hipStream_t s) {
     // Waves per workgroup: enough that the whole launch has ~24 waves per CU
-    // (6144 waves over 256 CUs), but at least one iteration per wave.
+    // (6144 waves over 256 CUs), but at least one iteration per wave.  The
+    // staged kernel also needs at most kStagedMaxIters iterations per wave.
     const uint32_t tiles = (uint32_t)div_up(n, kGemvCols);
     const uint32_t nb = k / 32;
+    const bool stageable = nb % kGemvBlocksPerIter == 0 &&
+                           nb <= (uint32_t)(kGemvMaxWaves * kStagedMaxIters * kGemvBlocksPerIter);
     uint32_t waves = (uint32_t)div_up(6144, tiles);
+    if (stageable) waves = max(waves, (uint32_t)div_up(nb, kStagedMaxIters * kGemvBlocksPerIter));
     waves = max(1u, min(waves, (uint32_t)kGemvMaxWaves));
     waves = min(waves, (uint32_t)div_up(nb, kGemvBlocksPerIter));
     uint32_t bpw = (uint32_t)div_up(nb, waves);
     bpw = (uint32_t)div_up(bpw, kGemvBlocksPerIter) * kGemvBlocksPerIter;
     waves = (uint32_t)div_up(nb, bpw);
+    if (stageable) {
+        const uint32_t lds = max(staged_geo(m, bpw).wave_bytes * waves, kRedBytes);
+        if (lds <= kLdsBytes) {
+            hipLaunchKernelGGL(gemv_staged_kernel, dim3(tiles), dim3(64 * waves), lds, s, a_i8, w_i8,
+                               a_scale, w_scale, out, m, n, k, bpw);
+            return hipGetLastError();
+        }
+    }
     if (nb % 4 == 0)
-        hipLaunchKernelGGL(gemv_kernel<true>, dim3(tiles), dim3(64 * waves), 0, s, a_i8, w_i8, a_scale,
-                           w_scale, out, m, n, k, bpw);
+        hipLaunchKernelGGL(gemv_direct_kernel<true>, dim3(tiles), dim3(64 * waves), 0, s, a_i8, w_i8,
+                           a_scale, w_scale, out, m, n, k, bpw);
     else
-        hipLaunchKernelGGL(gemv_kernel<false>, dim3(tiles), dim3(64 * waves), 0, s, a_i8, w_i8, a_scale,
-                           w_scale, out, m, n, k, bpw);
+        hipLaunchKernelGGL(gemv_direct_kernel<false>, dim3(tiles), dim3(64 * waves), 0, s, a_i8, w_i8,
+                           a_scale, w_scale, out, m, n, k, bpw);
     return hipGetLastError();
 }
 

@@ -45,9 +45,15 @@ def test_gemm_parity_random(m, n, k):
     _check(f"gemm {m}x{n}x{k}", host(out), y, t, k)
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 7, 8])
-def test_gemv_parity_random_and_against_gemm(m):
-    n, k = 333, 1056
+# K = 1056 (33 blocks) and 2400 (75): direct kernel with per-element scale
+# loads; 2176 (68 blocks, scale rows padded to 128 in LDS) and 4096: staged
+# kernel; m = 8 at K = 16384 needs 180 KB of LDS, so the direct kernel with
+# vector scale loads runs, while m = 1 at that K is staged.
+@pytest.mark.parametrize("m,k", [(1, 1056), (2, 1056), (3, 1056), (4, 1056), (5, 1056), (6, 1056),
+                                 (7, 1056), (8, 1056), (2, 2400), (1, 2176), (3, 2176), (8, 2176),
+                                 (5, 4096), (8, 4096), (1, 16384), (8, 16384)])
+def test_gemv_parity_random_and_against_gemm(m, k):
+    n = 333
     say(f"gemv m={m} n={n} k={k}")
     a, w, a_s, w_s = _rand_operands(100 + m, m, n, k, zero_frac=0.05)
     y, t = oracle.gemm_ref(a, w, a_s, w_s)
