@@ -13,9 +13,11 @@ namespace bsr {
 // 32-element block, 256 lanes per workgroup.
 constexpr int kRqaThreads = 256;
 constexpr int kRqaLanesPerBlock = 4;
+constexpr int kRqaUnroll = 2;        // chunks per lane, loads issued together
 // Weight requant: one lane per 32-element block (16 packed bytes in,
 // 32 int8 out), 256 lanes per workgroup.
 constexpr int kRqwThreads = 256;
+constexpr int kRqwUnroll = 2;        // blocks per lane, loads issued together
 
 // ---- GEMM (m > 8) ---------------------------------------------------------
 // A workgroup computes a BM x BN output tile; each wave owns a WM x WN piece

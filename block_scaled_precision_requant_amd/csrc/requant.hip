@@ -14,8 +14,9 @@
 //    A power-of-two s has an exact reciprocal (q0 is then exact); a subnormal
 //    s takes the IEEE divide and the clamp for the whole block.
 //  * NVFP4 path: a half-block holds one E4M3 scale, so its 16 elements take at
-//    most 8 magnitudes.  The 7 non-zero magnitudes of each half are divided
-//    (IEEE) once, and every element picks its code with a byte permute.
+//    most 8 magnitudes.  The 7 non-zero magnitudes of each half are quantized
+//    once (same reciprocal fast path, IEEE divide near ties and for subnormal
+//    s), and every element picks its code with a byte permute.
 #include "bsr_internal.h"
 
 namespace bsr {
@@ -35,15 +36,9 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
            ((uint32_t)d << 24);
 }
 
-__global__ __launch_bounds__(kRqaThreads) void requant_a_kernel(const uint4 *__restrict__ a,
-                                                                uint2 *__restrict__ q,
-                                                                float *__restrict__ scale,
-                                                                uint64_t nchunks) {
-    const uint64_t c = (uint64_t)blockIdx.x * kRqaThreads + threadIdx.x;
-    // nchunks is a multiple of 4 and so is every quad's first lane: a quad is
-    // either wholly live or wholly idle.
-    const bool live = c < nchunks;
-    const uint4 raw = live ? a[c] : make_uint4(0, 0, 0, 0);
+// Quantize one 16-byte chunk (8 BF16) of a block whose four chunks sit on the
+// four lanes of a quad; returns the 8 codes packed and the block scale.
+__device__ __forceinline__ uint2 requant_a_chunk(uint4 raw, float &s_out) {
     const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
     float v[8];
 #pragma unroll
@@ -82,10 +77,33 @@ __global__ __launch_bounds__(kRqaThreads) void requant_a_kernel(const uint4 *__r
                 if (near & (1u << i)) t[i] = rintf(v[i] / s);
         }
     }
-    if (live) {
-        q[c] = make_uint2(pack4_i8((int)t[0], (int)t[1], (int)t[2], (int)t[3]),
-                          pack4_i8((int)t[4], (int)t[5], (int)t[6], (int)t[7]));
-        if ((c & 3) == 0) scale[c >> 2] = s;
+    s_out = s;
+    return make_uint2(pack4_i8((int)t[0], (int)t[1], (int)t[2], (int)t[3]),
+                      pack4_i8((int)t[4], (int)t[5], (int)t[6], (int)t[7]));
+}
+
+// Each lane handles U chunks kRqaThreads apart (all U loads are issued before
+// any is used); a quad's four lanes always hold the four chunks of one block.
+template <int U>
+__global__ __launch_bounds__(kRqaThreads) void requant_a_kernel(const uint4 *__restrict__ a,
+                                                                uint2 *__restrict__ q,
+                                                                float *__restrict__ scale,
+                                                                uint64_t nchunks) {
+    const uint64_t base = (uint64_t)blockIdx.x * kRqaThreads * U + threadIdx.x;
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) raw[u] = a[min(base + (uint64_t)u * kRqaThreads, nchunks - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        // nchunks is a multiple of 4 and so is every quad's first chunk: a
+        // quad is either wholly live or wholly idle.
+        const uint64_t c = base + (uint64_t)u * kRqaThreads;
+        float s;
+        const uint2 packed = requant_a_chunk(raw[u], s);
+        if (c < nchunks) {
+            q[c] = packed;
+            if ((c & 3) == 0) scale[c >> 2] = s;
+        }
     }
 }
 
@@ -134,16 +152,26 @@ __device__ __forceinline__ uint2 lookup8(uint32_t w, uint32_t pos_lo, uint32_t p
                       __builtin_amdgcn_perm(od, ev, 0x07030602u));
 }
 
-__global__ __launch_bounds__(kRqwThreads) void requant_w_kernel(const uint4 *__restrict__ packed,
-                                                                const uint16_t *__restrict__ e4m3,
-                                                                float scale2,
-                                                                uint4 *__restrict__ q,
-                                                                float *__restrict__ scale,
-                                                                uint64_t nblocks) {
-    const uint64_t b = (uint64_t)blockIdx.x * kRqwThreads + threadIdx.x;
-    if (b >= nblocks) return;
-    const uint4 p = packed[b];
-    const uint32_t sc = e4m3[b];
+// Signed int8 code of v = fl32(fl32(mag * s16) * scale2) in a block of scale
+// s != 0: rne(fl32(v / s)), clamped (reachable only for subnormal s).  Normal
+// s uses the reciprocal fast path of the activation kernel: q0 = v * r with
+// r ~ 1/s (exact for a power of two) is within 2^-15 of v / s, so unless q0
+// is within 2^-14 of a half-integer its rounding is the quotient's.
+__device__ __forceinline__ int w_code(float v, float s, float r, bool exact_r, bool sub) {
+    float t;
+    if (sub) {
+        t = fminf(fmaxf(rintf(v / s), -127.0f), 127.0f);
+    } else {
+        const float q0 = v * r;
+        t = rintf(q0);
+        if (!exact_r && fabsf(q0 - t) > kTieGuard) t = rintf(v / s);
+    }
+    return (int)t;
+}
+
+// Quantize one 32-element block: 16 packed bytes and its two E4M3 scales.
+__device__ __forceinline__ void requant_w_block(uint4 p, uint32_t sc, float scale2, uint4 &lo,
+                                                uint4 &hi, float &s_out) {
     const float s16[2] = {e4m3_to_f32(sc & 0xFFu), e4m3_to_f32(sc >> 8)};
     const uint32_t mc[2] = {max_mag_code(p.x, p.y), max_mag_code(p.z, p.w)};
 
@@ -152,8 +180,13 @@ __global__ __launch_bounds__(kRqwThreads) void requant_w_kernel(const uint4 *__r
     for (int h = 0; h < 2; ++h) amax = fmaxf(amax, fabsf((e2m1_mag_to_f32(mc[h]) * s16[h]) * scale2));
     const float s = amax / 127.0f;
 
-    uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+    lo = make_uint4(0, 0, 0, 0);
+    hi = make_uint4(0, 0, 0, 0);
     if (s != 0.0f) {
+        const uint32_t sb = __float_as_uint(s);
+        const bool sub = s < 0x1p-126f;
+        const bool pow2 = (sb & 0x007FFFFFu) == 0;
+        const float r = pow2 ? __uint_as_float(0x7F000000u - (sb & 0x7F800000u)) : __builtin_amdgcn_rcpf(s);
         const float mags[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
         uint32_t tab[2][4];  // pos_lo, pos_hi, neg_lo, neg_hi per half
 #pragma unroll
@@ -161,10 +194,8 @@ __global__ __launch_bounds__(kRqwThreads) void requant_w_kernel(const uint4 *__r
             int qm[8];
             qm[0] = 0;
 #pragma unroll
-            for (int c = 1; c < 8; ++c) {
-                const float v = (mags[c] * s16[h]) * scale2;  // exact product, then one rounding
-                qm[c] = (int)fminf(fmaxf(rintf(v / s), -127.0f), 127.0f);
-            }
+            for (int c = 1; c < 8; ++c)
+                qm[c] = w_code((mags[c] * s16[h]) * scale2, s, r, pow2, sub);  // exact product, one rounding
             tab[h][0] = pack4_i8(qm[0], qm[1], qm[2], qm[3]);
             tab[h][1] = pack4_i8(qm[4], qm[5], qm[6], qm[7]);
             tab[h][2] = pack4_i8(-qm[0], -qm[1], -qm[2], -qm[3]);
@@ -177,9 +208,38 @@ __global__ __launch_bounds__(kRqwThreads) void requant_w_kernel(const uint4 *__r
         lo = make_uint4(e0.x, e0.y, e1.x, e1.y);
         hi = make_uint4(e2.x, e2.y, e3.x, e3.y);
     }
-    q[2 * b] = lo;
-    q[2 * b + 1] = hi;
-    scale[b] = s;
+    s_out = s;
+}
+
+// Each lane handles U blocks kRqwThreads apart, all loads issued first.
+template <int U>
+__global__ __launch_bounds__(kRqwThreads) void requant_w_kernel(const uint4 *__restrict__ packed,
+                                                                const uint16_t *__restrict__ e4m3,
+                                                                float scale2,
+                                                                uint4 *__restrict__ q,
+                                                                float *__restrict__ scale,
+                                                                uint64_t nblocks) {
+    const uint64_t base = (uint64_t)blockIdx.x * kRqwThreads * U + threadIdx.x;
+    uint4 p[U];
+    uint32_t sc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint64_t b = min(base + (uint64_t)u * kRqwThreads, nblocks - 1);
+        p[u] = packed[b];
+        sc[u] = e4m3[b];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint64_t b = base + (uint64_t)u * kRqwThreads;
+        uint4 lo, hi;
+        float s;
+        requant_w_block(p[u], sc[u], scale2, lo, hi, s);
+        if (b < nblocks) {
+            q[2 * b] = lo;
+            q[2 * b + 1] = hi;
+            scale[b] = s;
+        }
+    }
 }
 
 }  // namespace
@@ -187,8 +247,8 @@ __global__ __launch_bounds__(kRqwThreads) void requant_w_kernel(const uint4 *__r
 hipError_t launch_requant_a(const uint16_t *a_bf16, int8_t *a_i8, float *a_scale, uint64_t nblocks,
                             hipStream_t s) {
     const uint64_t nchunks = nblocks * kRqaLanesPerBlock;
-    const uint64_t grid = div_up(nchunks, kRqaThreads);
-    hipLaunchKernelGGL(requant_a_kernel, dim3((uint32_t)grid), dim3(kRqaThreads), 0, s,
+    const uint64_t grid = div_up(nchunks, (uint64_t)kRqaThreads * kRqaUnroll);
+    hipLaunchKernelGGL(requant_a_kernel<kRqaUnroll>, dim3((uint32_t)grid), dim3(kRqaThreads), 0, s,
                        reinterpret_cast<const uint4 *>(a_bf16), reinterpret_cast<uint2 *>(a_i8),
                        a_scale, nchunks);
     return hipGetLastError();
@@ -196,8 +256,8 @@ hipError_t launch_requant_a(const uint16_t *a_bf16, int8_t *a_i8, float *a_scale
 
 hipError_t launch_requant_w(const uint8_t *w_packed, const uint8_t *w_e4m3, float scale2,
                             int8_t *w_i8, float *w_scale, uint64_t nblocks, hipStream_t s) {
-    const uint64_t grid = div_up(nblocks, kRqwThreads);
-    hipLaunchKernelGGL(requant_w_kernel, dim3((uint32_t)grid), dim3(kRqwThreads), 0, s,
+    const uint64_t grid = div_up(nblocks, (uint64_t)kRqwThreads * kRqwUnroll);
+    hipLaunchKernelGGL(requant_w_kernel<kRqwUnroll>, dim3((uint32_t)grid), dim3(kRqwThreads), 0, s,
                        reinterpret_cast<const uint4 *>(w_packed),
                        reinterpret_cast<const uint16_t *>(w_e4m3), scale2,
                        reinterpret_cast<uint4 *>(w_i8), w_scale, nblocks);
