@@ -120,6 +120,32 @@ def workloads():
     return w
 
 
+@dataclass
+class SiluMulInput:
+    """The down projection's input before quantization: the gate and up halves
+    [M, I] of a gate+up GEMM output, as BF16 bits (gate ~ N(0, gate_scale^2),
+    up ~ N(0, 1), independent draws)."""
+    name: str
+    m: int
+    k: int
+    seed: int
+    tensor_base: int
+    gate_scale: float = 2.0
+
+    def gate(self, m=None):
+        m = self.m if m is None else m
+        return bf16_normal(rng_for(self.seed, self.tensor_base + 1), m, self.k, scale=self.gate_scale)
+
+    def up(self, m=None):
+        m = self.m if m is None else m
+        return bf16_normal(rng_for(self.seed, self.tensor_base + 2), m, self.k)
+
+
+def silu_mul_input():
+    """SiLU product feeding the dense FFN's down projection: M=4096, I=14336."""
+    return SiluMulInput("ffn_down_input", 4096, 14336, 2, 20)
+
+
 def workload(name):
     for w in workloads():
         if w.name == name:

@@ -53,6 +53,14 @@ def lib():
         L.orc_requant_w.argtypes = [_u8p, _u8p, ctypes.c_float, _i8p, _f32p, _i64, _i64]
         L.orc_requant_a.restype = ctypes.c_int
         L.orc_requant_a.argtypes = [_u16p, _i8p, _f32p, _i64, _i64]
+        L.orc_bf16_round.restype = ctypes.c_float
+        L.orc_bf16_round.argtypes = [ctypes.c_float]
+        L.orc_exp_neg_f32.restype = ctypes.c_float
+        L.orc_exp_neg_f32.argtypes = [ctypes.c_float]
+        L.orc_silu_mul.restype = ctypes.c_float
+        L.orc_silu_mul.argtypes = [ctypes.c_float, ctypes.c_float]
+        L.orc_silu_mul_requant.restype = ctypes.c_int
+        L.orc_silu_mul_requant.argtypes = [_u16p, _u16p, _i64, _i8p, _f32p, _i64, _i64]
         L.orc_block_partials.restype = ctypes.c_int
         L.orc_block_partials.argtypes = [_i8p, _i8p, _i32p, _i64, _i64, _i64]
         L.orc_gemm_ref.restype = ctypes.c_int
@@ -109,6 +117,37 @@ def requant_a(a_bf16_bits):
     rc = lib().orc_requant_a(_ptr(a, _u16p), _ptr(a_i8, _i8p), _ptr(a_scale, _f32p), m, k)
     _check(rc, "requant_a")
     return a_i8, a_scale
+
+
+def bf16_round(x: float) -> float:
+    """Nearest BF16 value of a binary32 (ties to even), as a float."""
+    return float(lib().orc_bf16_round(float(np.float32(x))))
+
+
+def exp_neg_f32(g: float) -> float:
+    """exp(-g) rounded once to binary32."""
+    return float(lib().orc_exp_neg_f32(float(np.float32(g))))
+
+
+def silu_mul(g: float, u: float) -> float:
+    """BF16 value of fl32(fl32(g / fl32(1 + exp(-g))) * u)."""
+    return float(lib().orc_silu_mul(float(np.float32(g)), float(np.float32(u))))
+
+
+def silu_mul_requant(gate_bits, up_bits, k=None):
+    """SiLU(gate) * up (BF16 raw bits, [M, ld]) over the first k columns ->
+    (q [M,k] int8, scale [M,k/32] float32)."""
+    g = np.ascontiguousarray(gate_bits, dtype=np.uint16)
+    u = np.ascontiguousarray(up_bits, dtype=np.uint16)
+    if g.shape != u.shape:
+        raise ValueError(f"gate {g.shape} and up {u.shape} differ")
+    m, ld = g.shape
+    k = ld if k is None else k
+    q = np.empty((m, k), np.int8)
+    s = np.empty((m, max(k // 32, 0)), np.float32)
+    rc = lib().orc_silu_mul_requant(_ptr(g, _u16p), _ptr(u, _u16p), ld, _ptr(q, _i8p), _ptr(s, _f32p), m, k)
+    _check(rc, "silu_mul_requant")
+    return q, s
 
 
 def block_partials(a_i8, w_i8):

@@ -173,6 +173,71 @@ int orc_requant_a(const uint16_t *a_bf16, int8_t *a_i8, float *a_scale, int64_t 
     return status;
 }
 
+/* ---- f1: SiLU(gate) * up, rounded to BF16, then the per-32 quantizer. ----
+ * The pages name a quantizer of a SiLU product (`W8a8Kernels::quant_silu` on
+ * page "metrale_model_layers/layers/ops/w8a8_decode/parts.rs", and the
+ * re-quantized SiLU product between gate+up and down in the module comment of
+ * page "metrale_model_layers/layers/ops/fp8_moe_grouped_tc_w8a8.rs")
+ * without fixing its arithmetic.  Reading taken here, for BF16 gate g and up u
+ * (widened exactly):
+ *   e = exp(-g) correctly rounded to binary32 (evaluated in binary64, rounded once),
+ *   silu = fl32(g / fl32(1 + e)),   h = bf16_rne(fl32(silu * u)),
+ * and the 32-blocks of h are quantized exactly as the activation requant does,
+ * so the fused step equals "SiLU·mul to BF16, then requant". */
+
+/* Round a binary32 to the nearest BF16 value (8 significant bits), ties to
+ * even, by rescaling the significand: no bit manipulation of the encoding. */
+static float round_to_bf16(float x)
+{
+    if (x == 0.0f || !isfinite(x))
+        return x;
+    if (fabsf(x) < ldexpf(1.0f, -126)) /* BF16 subnormal grid: multiples of 2^-133 */
+        return ldexpf(nearbyintf(ldexpf(x, 133)), -133);
+    int e;
+    float m = frexpf(x, &e); /* x = m * 2^e, 0.5 <= |m| < 1 */
+    return ldexpf(nearbyintf(ldexpf(m, 8)), e - 8);
+}
+
+float orc_bf16_round(float x) { return round_to_bf16(x); }
+
+/* exp(-g) rounded once to binary32 */
+float orc_exp_neg_f32(float g) { return (float)exp(-(double)g); }
+
+float orc_silu_mul(float g, float u)
+{
+    float e = orc_exp_neg_f32(g);
+    float d = 1.0f + e;
+    float silu = g / d;
+    return round_to_bf16(silu * u);
+}
+
+/* gate, up: [m, ld] BF16 bits (the first k of each row are used);
+ * q [m, k] i8 and scale [m, k/32] f32, dense. */
+int orc_silu_mul_requant(const uint16_t *gate, const uint16_t *up, int64_t ld, int8_t *q,
+                         float *scale, int64_t m, int64_t k)
+{
+    if (k <= 0 || k % 32 != 0 || ld < k)
+        return ORC_EK;
+    int status = ORC_OK;
+    const int64_t nb = k / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < m; ++row) {
+        float v[32];
+        for (int64_t b = 0; b < nb; ++b) {
+            for (int j = 0; j < 32; ++j) {
+                int64_t idx = row * ld + 32 * b + j;
+                v[j] = orc_silu_mul(bf16_to_f32(gate[idx]), bf16_to_f32(up[idx]));
+            }
+            int rc = quantize_block32(v, q + row * k + 32 * b, scale + row * nb + b);
+            if (rc != ORC_OK) {
+#pragma omp atomic write
+                status = rc;
+            }
+        }
+    }
+    return status;
+}
+
 /* ---- O5: exact int32 block partials P[m, n, k/32]. --------------------- */
 int orc_block_partials(const int8_t *a_i8, const int8_t *w_i8, int32_t *p,
                        int64_t m, int64_t n, int64_t k)
