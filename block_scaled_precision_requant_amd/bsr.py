@@ -24,6 +24,7 @@ SIGNATURES = {
     "requant_a_int8": (_int, [_vp, _vp, _vp, _u32, _u32, _vp]),
     "int8_gemm_blockscaled": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u32, _u32, _vp]),
     "int8_gemm_blockscaled_ex": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u32, _u32, _vp, _int]),
+    "silu_mul_requant_int8": (_int, [_vp, _vp, _u32, _vp, _vp, _u32, _u32, _vp]),
     "bsr_status_string": (ctypes.c_char_p, [_int]),
 }
 
@@ -102,6 +103,27 @@ def requant_a_int8(a_bf16, a_i8, a_scale, stream=None):
     _shape(a_scale, (m, k // 32), "a_scale")
     st = lib().requant_a_int8(_ptr(a_bf16), _ptr(a_i8), _ptr(a_scale), m, k, _stream(stream, a_i8))
     _done(st, "requant_a_int8")
+
+
+def silu_mul_requant_int8(gate, up, a_i8, a_scale, stream=None):
+    """SiLU(gate) * up -> a_i8 [M,K] int8 and a_scale [M,K/32] float32.
+
+    gate and up are [M,K] BF16 (raw 16-bit) views with unit column stride and
+    the same row stride (for instance the two halves of one [M, 2K] buffer)."""
+    m, k = gate.shape
+    if tuple(up.shape) != (m, k):
+        raise ValueError(f"up: shape {tuple(up.shape)}, expected {(m, k)}")
+    for t, what in ((gate, "gate"), (up, "up")):
+        if not t.is_cuda:
+            raise ValueError(f"{what}: must be a device tensor")
+        if t.element_size() != 2 or (m > 1 and t.stride(1) != 1) or (m > 1 and t.stride(0) != gate.stride(0)):
+            raise ValueError(f"{what}: 16-bit rows with unit column stride and the gate's row stride")
+    ld = gate.stride(0) if m > 1 else k
+    _shape(a_i8, (m, k), "a_i8")
+    _shape(a_scale, (m, k // 32), "a_scale")
+    st = lib().silu_mul_requant_int8(_ptr(gate), _ptr(up), ld, _ptr(a_i8), _ptr(a_scale), m, k,
+                                     _stream(stream, a_i8))
+    _done(st, "silu_mul_requant_int8")
 
 
 def int8_gemm_blockscaled_ex(a_i8, w_i8, a_scale, w_scale, out, path=PATH_AUTO, stream=None):

@@ -82,6 +82,19 @@ int requant_a_int8(const uint16_t *a_bf16, int8_t *a_i8, float *a_scale, uint32_
     return launched(bsr::launch_requant_a(a_bf16, a_i8, a_scale, nblocks, static_cast<hipStream_t>(stream)));
 }
 
+int silu_mul_requant_int8(const uint16_t *gate, const uint16_t *up, uint32_t ld, int8_t *a_i8,
+                          float *a_scale, uint32_t m, uint32_t k, void *stream) {
+    if (!k_ok(k) || ld < k || ld % 8 != 0) return BSR_EINVAL;
+    if (m == 0) return BSR_OK;
+    if (!gate || !up || !a_i8 || !a_scale) return BSR_ENULL;
+    if (!aligned(gate, 16) || !aligned(up, 16) || !aligned(a_i8, 16) || !aligned(a_scale, 4))
+        return BSR_EALIGN;
+    const uint64_t nchunks = (uint64_t)m * (k / 8);
+    if (bsr::div_up(nchunks, bsr::kRqaThreads) > kMaxGrid) return BSR_EINVAL;
+    if (int st = check_device()) return st;
+    return launched(bsr::launch_silu_requant(gate, up, ld, a_i8, a_scale, m, k, static_cast<hipStream_t>(stream)));
+}
+
 int int8_gemm_blockscaled_ex(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
                              const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                              void *stream, int path) {

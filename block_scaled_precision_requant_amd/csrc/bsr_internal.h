@@ -56,6 +56,8 @@ hipError_t launch_requant_w(const uint8_t *w_packed, const uint8_t *w_e4m3, floa
                             int8_t *w_i8, float *w_scale, uint64_t nblocks, hipStream_t s);
 hipError_t launch_requant_a(const uint16_t *a_bf16, int8_t *a_i8, float *a_scale,
                             uint64_t nblocks, hipStream_t s);
+hipError_t launch_silu_requant(const uint16_t *gate, const uint16_t *up, uint32_t ld, int8_t *a_i8,
+                               float *a_scale, uint32_t m, uint32_t k, hipStream_t s);
 hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
                        const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
                        uint32_t k, hipStream_t s);

@@ -107,6 +107,57 @@ __global__ __launch_bounds__(kRqaThreads) void requant_a_kernel(const uint4 *__r
     }
 }
 
+// ---- fused SiLU·mul -> int8 per-32 (the down projection's input) ----------
+// The pages' SiLU-product quantizer (`W8a8Kernels::quant_silu`, page
+// "metrale_model_layers/layers/ops/w8a8_decode/parts.rs") feeds the int8
+// per-32 quantizer above: h = bf16_rne(fl32(fl32(g / fl32(1 + e)) * u)) with
+// e = exp(-g) rounded once to binary32 from a binary64 evaluation, then the
+// 32-blocks of h are quantized exactly like BF16 activations.
+
+__device__ __forceinline__ uint32_t silu_mul_bf16(uint32_t g_bits, uint32_t u_bits) {
+    const float g = __uint_as_float(g_bits << 16), u = __uint_as_float(u_bits << 16);
+    const float e = (float)exp(-(double)g);
+    const float silu = g / (1.0f + e);
+    return f32_to_bf16_rne(silu * u);
+}
+
+// Each lane handles U 8-element chunks kRqaThreads apart (loads first); chunk
+// c of the dense output is row c / kc, columns 8 * (c % kc) .. + 7 of the
+// inputs (kc = k / 8 chunks per row, input rows ld elements apart).
+template <int U>
+__global__ __launch_bounds__(kRqaThreads) void silu_requant_kernel(const uint16_t *__restrict__ gate,
+                                                                   const uint16_t *__restrict__ up,
+                                                                   uint32_t ld, uint2 *__restrict__ q,
+                                                                   float *__restrict__ scale,
+                                                                   uint64_t nchunks, uint32_t kc) {
+    const uint64_t base = (uint64_t)blockIdx.x * kRqaThreads * U + threadIdx.x;
+    uint4 gr[U], ur[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint64_t c = min(base + (uint64_t)u * kRqaThreads, nchunks - 1);
+        const uint64_t off = (c / kc) * ld + (c % kc) * 8;
+        gr[u] = *reinterpret_cast<const uint4 *>(gate + off);
+        ur[u] = *reinterpret_cast<const uint4 *>(up + off);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint64_t c = base + (uint64_t)u * kRqaThreads;
+        const uint32_t gw[4] = {gr[u].x, gr[u].y, gr[u].z, gr[u].w};
+        const uint32_t uw[4] = {ur[u].x, ur[u].y, ur[u].z, ur[u].w};
+        uint32_t hw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)   // element 2i in the low half of word i
+            hw[i] = silu_mul_bf16(gw[i] & 0xFFFFu, uw[i] & 0xFFFFu) |
+                    (silu_mul_bf16(gw[i] >> 16, uw[i] >> 16) << 16);
+        float s;
+        const uint2 packed = requant_a_chunk(make_uint4(hw[0], hw[1], hw[2], hw[3]), s);
+        if (c < nchunks) {
+            q[c] = packed;
+            if ((c & 3) == 0) scale[c >> 2] = s;
+        }
+    }
+}
+
 // OCP E4M3 code -> binary32.  Its exponent and mantissa bits shifted into a
 // binary32 give the value times 2^-120 (E4M3 subnormals land on binary32
 // subnormals), so one exact multiply restores it.
@@ -251,6 +302,16 @@ hipError_t launch_requant_a(const uint16_t *a_bf16, int8_t *a_i8, float *a_scale
     hipLaunchKernelGGL(requant_a_kernel<kRqaUnroll>, dim3((uint32_t)grid), dim3(kRqaThreads), 0, s,
                        reinterpret_cast<const uint4 *>(a_bf16), reinterpret_cast<uint2 *>(a_i8),
                        a_scale, nchunks);
+    return hipGetLastError();
+}
+
+hipError_t launch_silu_requant(const uint16_t *gate, const uint16_t *up, uint32_t ld, int8_t *a_i8,
+                               float *a_scale, uint32_t m, uint32_t k, hipStream_t s) {
+    const uint32_t kc = k / 8;
+    const uint64_t nchunks = (uint64_t)m * kc;
+    const uint64_t grid = div_up(nchunks, (uint64_t)kRqaThreads * kRqaUnroll);
+    hipLaunchKernelGGL(silu_requant_kernel<kRqaUnroll>, dim3((uint32_t)grid), dim3(kRqaThreads), 0, s,
+                       gate, up, ld, reinterpret_cast<uint2 *>(a_i8), a_scale, nchunks, kc);
     return hipGetLastError();
 }
 

@@ -124,6 +124,28 @@ int int8_gemm_blockscaled_ex(const int8_t *a_i8, const int8_t *w_i8, const float
                              const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
                              uint32_t k, void *stream, int path);
 
+/*
+ * Fused SiLU·mul -> int8 per-32 requant: the quantized input of the down
+ * projection, straight from the gate and up halves of a gate+up output (the
+ * SiLU-product quantizer `W8a8Kernels::quant_silu` of page
+ * "metrale_model_layers/layers/ops/w8a8_decode/parts.rs" and the re-quantized
+ * SiLU product of page ".../fp8_moe_grouped_tc_w8a8.rs", here with the int8
+ * per-32 quantizer of step 2).
+ *   gate, up [m, ld] BF16 as raw u16, 16-byte aligned; columns 0..k-1 of each
+ *            row are used (ld >= k, ld a multiple of 8).  Both halves of one
+ *            [m, 2I] buffer qualify: gate = buf, up = buf + I, ld = 2I.
+ *   a_i8     [m, k]    i8 output, dense, 16-byte aligned
+ *   a_scale  [m, k/32] f32 output, dense, 4-byte aligned
+ * Per element: e = exp(-g) rounded once to binary32 (evaluated in binary64),
+ * h = bf16_rne(fl32(fl32(g / fl32(1 + e)) * u)); then the quantizer above on
+ * the 32-blocks of h, so the result equals requant_a_int8 applied to the BF16
+ * SiLU product.  (Where exp(-g) overflows binary32, g < -88.72, silu is -0.)
+ * Errors: BSR_EINVAL (k, ld < k, ld not a multiple of 8), BSR_ENULL,
+ * BSR_EALIGN, BSR_EDEVICE, BSR_ELAUNCH.
+ */
+int silu_mul_requant_int8(const uint16_t *gate, const uint16_t *up, uint32_t ld, int8_t *a_i8,
+                          float *a_scale, uint32_t m, uint32_t k, void *stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *bsr_status_string(int status);
 

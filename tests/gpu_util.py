@@ -56,3 +56,12 @@ def host(t):
 
 def f32_bits(x):
     return np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+
+
+def gpu_silu_requant(gate_bits, up_bits):
+    g, u = to_dev(gate_bits.view(np.int16)), to_dev(up_bits.view(np.int16))
+    m, k = g.shape
+    q = torch.empty((m, k), dtype=torch.int8, device=DEV)
+    s = torch.empty((m, k // 32), dtype=torch.float32, device=DEV)
+    bsr.silu_mul_requant_int8(g, u, q, s)
+    return q, s

@@ -77,6 +77,18 @@ def test_null_and_alignment_errors():
     assert L.int8_gemm_blockscaled(FAKE, FAKE, FAKE, FAKE, null, 4, 4, 64, None) == bsr.BSR_ENULL
 
 
+def test_silu_requant_validation():
+    L = bsr.lib()
+    null = ctypes.c_void_p(0)
+    assert L.silu_mul_requant_int8(FAKE, FAKE, 64, FAKE, FAKE, 4, 48, None) == bsr.BSR_EINVAL   # k
+    assert L.silu_mul_requant_int8(FAKE, FAKE, 32, FAKE, FAKE, 4, 64, None) == bsr.BSR_EINVAL   # ld < k
+    assert L.silu_mul_requant_int8(FAKE, FAKE, 68, FAKE, FAKE, 4, 64, None) == bsr.BSR_EINVAL   # ld % 8
+    assert L.silu_mul_requant_int8(FAKE, FAKE, 64, FAKE, FAKE, 0, 64, None) == bsr.BSR_OK       # empty
+    assert L.silu_mul_requant_int8(null, FAKE, 64, FAKE, FAKE, 4, 64, None) == bsr.BSR_ENULL
+    assert L.silu_mul_requant_int8(FAKE, _fake(8), 64, FAKE, FAKE, 4, 64, None) == bsr.BSR_EALIGN
+    assert L.silu_mul_requant_int8(FAKE, FAKE, 64, FAKE, _fake(2), 4, 64, None) == bsr.BSR_EALIGN
+
+
 def test_bad_scale2_and_path():
     L = bsr.lib()
     for s2 in (float("nan"), float("inf"), -float("inf")):
