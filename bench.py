@@ -46,7 +46,7 @@ def _args():
     p.add_argument("--decode-iters", type=int, default=100)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
-    p.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
+    p.add_argument("--only", choices=["all", "prefill", "decode", "silu", "copy"], default="all",
                    help="copy: a plain 256 MiB device copy, the known-size reference for HBM byte counters")
     return p.parse_args()
 
@@ -242,6 +242,25 @@ def main():
         rec["decode"] = dict(cases=dec, gemv_gbs_mean=float(np.mean(gbs)),
                              gemv_frac_hbm_mean=float(np.mean(gbs)) / PEAK_HBM_GBS)
 
+    # ------------------------------------------------------------ fused SiLU requant
+    if args.only in ("all", "silu"):
+        src = inputs.silu_mul_input()
+        g_bits, u_bits = src.gate(), src.up()
+        sbytes = src.m * src.k * (2 + 2 + 1 + 1 / 8)
+        nset = max(2, int(np.ceil(2 ** 30 / sbytes)))
+        ssets = [dict(g=dev_t(g_bits.view(np.int16)), u=dev_t(u_bits.view(np.int16)),
+                      q=torch.empty((src.m, src.k), dtype=torch.int8, device=dev),
+                      s=torch.empty((src.m, src.k // 32), dtype=torch.float32, device=dev))
+                 for _ in range(nset)]
+        t_s = burst(lambda i: bsr.silu_mul_requant_int8(ssets[i % nset]["g"], ssets[i % nset]["u"],
+                                                        ssets[i % nset]["q"], ssets[i % nset]["s"],
+                                                        stream=stream), max(10, 2 * nset))
+        rec["silu"] = dict(workload=f"SiLU(gate) * up -> int8 per 32, M={src.m} I={src.k}",
+                           us_burst=t_s * 1e6, gbs=sbytes / t_s / 1e9,
+                           frac_hbm=sbytes / t_s / 1e9 / PEAK_HBM_GBS)
+        del ssets
+        torch.cuda.empty_cache()
+
     # ------------------------------------------------------------ CPU oracle
     cpu = None
     if not args.no_cpu_baseline and args.only in ("all", "prefill"):
@@ -299,6 +318,8 @@ def main():
         line["cpu_baseline"] = cpu
     if "decode" in rec:
         line["decode"] = rec["decode"]
+    if "silu" in rec:
+        line["silu_mul_requant"] = rec["silu"]
     print(json.dumps(line), flush=True)
 
 

@@ -36,16 +36,9 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
            ((uint32_t)d << 24);
 }
 
-// Quantize one 16-byte chunk (8 BF16) of a block whose four chunks sit on the
-// four lanes of a quad; returns the 8 codes packed and the block scale.
-__device__ __forceinline__ uint2 requant_a_chunk(uint4 raw, float &s_out) {
-    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __uint_as_float(wd[i] << 16);
-        v[2 * i + 1] = __uint_as_float(wd[i] & 0xFFFF0000u);
-    }
+// Quantize 8 values (BF16-representable) of a block whose 32 values sit on
+// the four lanes of a quad; returns the 8 codes packed and the block scale.
+__device__ __forceinline__ uint2 requant_a_vals(const float (&v)[8], float &s_out) {
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -82,6 +75,18 @@ __device__ __forceinline__ uint2 requant_a_chunk(uint4 raw, float &s_out) {
                       pack4_i8((int)t[4], (int)t[5], (int)t[6], (int)t[7]));
 }
 
+// One 16-byte chunk (8 BF16, element 2i in the low half of word i).
+__device__ __forceinline__ uint2 requant_a_chunk(uint4 raw, float &s_out) {
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(wd[i] << 16);
+        v[2 * i + 1] = __uint_as_float(wd[i] & 0xFFFF0000u);
+    }
+    return requant_a_vals(v, s_out);
+}
+
 // Each lane handles U chunks kRqaThreads apart (all U loads are issued before
 // any is used); a quad's four lanes always hold the four chunks of one block.
 template <int U>
@@ -114,16 +119,74 @@ __global__ __launch_bounds__(kRqaThreads) void requant_a_kernel(const uint4 *__r
 // e = exp(-g) rounded once to binary32 from a binary64 evaluation, then the
 // 32-blocks of h are quantized exactly like BF16 activations.
 
-__device__ __forceinline__ uint32_t silu_mul_bf16(uint32_t g_bits, uint32_t u_bits) {
-    const float g = __uint_as_float(g_bits << 16), u = __uint_as_float(u_bits << 16);
+__device__ __forceinline__ float silu32(float g) {
     const float e = (float)exp(-(double)g);
-    const float silu = g / (1.0f + e);
-    return f32_to_bf16_rne(silu * u);
+    return g / (1.0f + e);
 }
 
-// Each lane handles U 8-element chunks kRqaThreads apart (loads first); chunk
-// c of the dense output is row c / kc, columns 8 * (c % kc) .. + 7 of the
-// inputs (kc = k / 8 chunks per row, input rows ld elements apart).
+__device__ __forceinline__ uint32_t silu_mul_bf16(uint32_t g_bits, uint32_t u_bits) {
+    const float g = __uint_as_float(g_bits << 16), u = __uint_as_float(u_bits << 16);
+    return f32_to_bf16_rne(silu32(g) * u);
+}
+
+// SiLU by table.  silu32 depends only on the 16-bit gate, and outside a band
+// it has a closed form:
+//   |g| < 2^-25:  exp(-g) rounds to 1, so silu32(g) = g / 2 (exact, = g * 0.5);
+//   g >= 32:      1 + exp(-g) rounds to 1, so silu32(g) = g;
+//   g <= -128:    exp(-g) overflows binary32, so silu32(g) = g / inf = -0.
+// The band -- positive gates with exponent -25..4, negative ones with -25..6 --
+// is 62 binades x 128 BF16 values, tabulated with silu32 itself.
+constexpr int kSiluPosBinades = 30, kSiluNegBinades = 32;
+constexpr int kSiluTable = (kSiluPosBinades + kSiluNegBinades) * 128;
+constexpr uint32_t kSiluLoExp = 127 - 25;  // biased exponent of the band's lowest binade
+
+__device__ __forceinline__ uint32_t silu_table_bits(int i) {  // BF16 gate of table entry i
+    const bool neg = i >= kSiluPosBinades * 128;
+    const int j = neg ? i - kSiluPosBinades * 128 : i;
+    return (neg ? 0x8000u : 0u) | ((kSiluLoExp + j / 128) << 7) | (uint32_t)(j % 128);
+}
+
+// b: BF16 gate bits (16 bits).  key = magnitude bits; the band is keys
+// [lo, pos_hi) for positive gates and [lo, neg_hi) for negative ones.
+__device__ __forceinline__ float silu_lookup(uint32_t b, const float *tab) {
+    constexpr uint32_t lo = kSiluLoExp << 7;
+    constexpr uint32_t pos_hi = (kSiluLoExp + kSiluPosBinades) << 7, neg_hi = (kSiluLoExp + kSiluNegBinades) << 7;
+    const uint32_t key = b & 0x7FFFu;
+    const bool neg = b >> 15;
+    const uint32_t hi = neg ? neg_hi : pos_hi;
+    const uint32_t idx = min(max(key, lo), hi - 1) - lo + (neg ? kSiluPosBinades * 128 : 0);
+    const float t = tab[idx];
+    const float g = __uint_as_float(b << 16);
+    if (key < lo) return g * 0.5f;
+    if (key >= hi) return neg ? -0.0f : g;
+    return t;
+}
+
+// binary32 -> the nearest BF16 value (ties to even), kept as a binary32.
+__device__ __forceinline__ float round_bf16(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return __uint_as_float((u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u);
+}
+
+// SiLU(gate) * up of one chunk, rounded to BF16 values.
+__device__ __forceinline__ void silu_mul_chunk(uint4 gr, uint4 ur, const float *tab, float (&h)[8]) {
+    const uint32_t gw[4] = {gr.x, gr.y, gr.z, gr.w};
+    const uint32_t uw[4] = {ur.x, ur.y, ur.z, ur.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // element 2i in the low half of word i
+        h[2 * i] = round_bf16(silu_lookup(gw[i] & 0xFFFFu, tab) * __uint_as_float(uw[i] << 16));
+        h[2 * i + 1] = round_bf16(silu_lookup(gw[i] >> 16, tab) * __uint_as_float(uw[i] & 0xFFFF0000u));
+    }
+}
+
+// Offset of chunk c (8 elements) in the gate / up rows: row c / kc, columns
+// 8 * (c % kc) .. + 7, rows ld elements apart.
+__device__ __forceinline__ uint64_t silu_chunk_offset(uint64_t c, uint32_t kc, uint32_t ld) {
+    return (c / kc) * ld + (c % kc) * 8;
+}
+
+// Direct kernel (small inputs): each lane handles U chunks kRqaThreads apart,
+// loads first, SiLU evaluated per element.
 template <int U>
 __global__ __launch_bounds__(kRqaThreads) void silu_requant_kernel(const uint16_t *__restrict__ gate,
                                                                    const uint16_t *__restrict__ up,
@@ -134,8 +197,7 @@ __global__ __launch_bounds__(kRqaThreads) void silu_requant_kernel(const uint16_
     uint4 gr[U], ur[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const uint64_t c = min(base + (uint64_t)u * kRqaThreads, nchunks - 1);
-        const uint64_t off = (c / kc) * ld + (c % kc) * 8;
+        const uint64_t off = silu_chunk_offset(min(base + (uint64_t)u * kRqaThreads, nchunks - 1), kc, ld);
         gr[u] = *reinterpret_cast<const uint4 *>(gate + off);
         ur[u] = *reinterpret_cast<const uint4 *>(up + off);
     }
@@ -154,6 +216,58 @@ __global__ __launch_bounds__(kRqaThreads) void silu_requant_kernel(const uint16_
         if (c < nchunks) {
             q[c] = packed;
             if ((c & 3) == 0) scale[c >> 2] = s;
+        }
+    }
+}
+
+// Table kernel (large inputs): persistent workgroups each fill the SiLU table
+// in LDS once, then stride over groups of kSiluThreads * U chunks.  Each lane
+// tracks the (row, column) of its chunks incrementally instead of dividing.
+template <int U>
+__global__ __launch_bounds__(kSiluThreads) void silu_requant_table_kernel(
+    const uint16_t *__restrict__ gate, const uint16_t *__restrict__ up, uint32_t ld,
+    uint2 *__restrict__ q, float *__restrict__ scale, uint64_t nchunks, uint32_t kc) {
+    __shared__ float tab[kSiluTable];
+    for (int i = threadIdx.x; i < kSiluTable; i += kSiluThreads)
+        tab[i] = silu32(__uint_as_float(silu_table_bits(i) << 16));
+    __syncthreads();
+    const uint64_t stride = (uint64_t)gridDim.x * kSiluThreads * U;
+    const uint64_t s_row = stride / kc;
+    const uint32_t s_col = (uint32_t)(stride % kc);
+    const uint64_t last = silu_chunk_offset(nchunks - 1, kc, ld);
+    uint64_t row[U];
+    uint32_t col[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint64_t c = (uint64_t)blockIdx.x * kSiluThreads * U + u * kSiluThreads + threadIdx.x;
+        row[u] = c / kc;
+        col[u] = (uint32_t)(c % kc);
+    }
+    for (uint64_t g0 = (uint64_t)blockIdx.x * kSiluThreads * U; g0 < nchunks; g0 += stride) {
+        uint4 gr[U], ur[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t c = g0 + u * kSiluThreads + threadIdx.x;
+            const uint64_t off = c < nchunks ? row[u] * ld + col[u] * 8 : last;
+            gr[u] = *reinterpret_cast<const uint4 *>(gate + off);
+            ur[u] = *reinterpret_cast<const uint4 *>(up + off);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t c = g0 + u * kSiluThreads + threadIdx.x;
+            float h[8], s;
+            silu_mul_chunk(gr[u], ur[u], tab, h);
+            const uint2 packed = requant_a_vals(h, s);
+            if (c < nchunks) {
+                q[c] = packed;
+                if ((c & 3) == 0) scale[c >> 2] = s;
+            }
+            col[u] += s_col;
+            row[u] += s_row;
+            if (col[u] >= kc) {
+                col[u] -= kc;
+                ++row[u];
+            }
         }
     }
 }
@@ -309,9 +423,19 @@ hipError_t launch_silu_requant(const uint16_t *gate, const uint16_t *up, uint32_
                                float *a_scale, uint32_t m, uint32_t k, hipStream_t s) {
     const uint32_t kc = k / 8;
     const uint64_t nchunks = (uint64_t)m * kc;
-    const uint64_t grid = div_up(nchunks, (uint64_t)kRqaThreads * kRqaUnroll);
-    hipLaunchKernelGGL(silu_requant_kernel<kRqaUnroll>, dim3((uint32_t)grid), dim3(kRqaThreads), 0, s,
-                       gate, up, ld, reinterpret_cast<uint2 *>(a_i8), a_scale, nchunks, kc);
+    // Table kernel once there is work for at least one workgroup per CU with
+    // 4 passes each (its table costs ~16 SiLU evaluations per lane); up to 4
+    // workgroups of 8 waves per CU (LDS: 31 KB each).
+    const uint64_t per_wg = (uint64_t)kSiluThreads * kSiluUnroll;
+    const uint64_t table_grid = min(div_up(nchunks, per_wg * 4), (uint64_t)4 * kGemmCus);
+    if (table_grid >= (uint64_t)kGemmCus) {
+        hipLaunchKernelGGL(silu_requant_table_kernel<kSiluUnroll>, dim3((uint32_t)table_grid), dim3(kSiluThreads),
+                           0, s, gate, up, ld, reinterpret_cast<uint2 *>(a_i8), a_scale, nchunks, kc);
+    } else {
+        const uint64_t grid = div_up(nchunks, (uint64_t)kRqaThreads * kRqaUnroll);
+        hipLaunchKernelGGL(silu_requant_kernel<kRqaUnroll>, dim3((uint32_t)grid), dim3(kRqaThreads), 0, s,
+                           gate, up, ld, reinterpret_cast<uint2 *>(a_i8), a_scale, nchunks, kc);
+    }
     return hipGetLastError();
 }
 

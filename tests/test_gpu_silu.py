@@ -19,19 +19,21 @@ def _same(name, q, s, q_ref, s_ref):
     assert bad_q == 0 and bad_s == 0
 
 
-def test_every_finite_bf16_gate():
+# 128 x 512 runs the per-element kernel; 1024 x 4096 (4.2 M elements) the
+# LDS-table kernel, whose closed-form ranges and every table entry are hit.
+@pytest.mark.parametrize("m,k", [(128, 512), (1024, 4096)])
+def test_every_finite_bf16_gate(m, k):
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     bits = bits[((bits >> 7) & 0xFF) != 0xFF]
-    k = 512
-    m = -(-bits.size // k)
-    gate = np.zeros(m * k, np.uint16)
-    gate[:bits.size] = np.random.default_rng(1).permutation(bits)
-    gate = gate.reshape(m, k)
+    rng = np.random.default_rng(1)
+    fill = rng.choice(bits, size=m * k - bits.size)
+    gate = rng.permutation(np.concatenate([bits, fill])).reshape(m, k)
+    assert np.unique(gate).size == bits.size
     # |up| <= 1/2 keeps silu(g) * up finite in BF16 for the largest gates
     up = inputs.f32_to_bf16_bits(np.random.default_rng(2).uniform(-0.5, 0.5, (m, k)).astype(np.float32))
     q_ref, s_ref = oracle.silu_mul_requant(gate, up)
     q, s = gpu_silu_requant(gate, up)
-    _same("all BF16 gates", host(q), host(s), q_ref, s_ref)
+    _same(f"all BF16 gates {m}x{k}", host(q), host(s), q_ref, s_ref)
 
 
 @pytest.mark.parametrize("m,k", [(1, 32), (3, 96), (7, 2080), (129, 1024)])
@@ -53,10 +55,10 @@ def test_workload_full():
     _same("ffn_down_input", host(q), host(s), q_ref, s_ref)
 
 
-def test_halves_of_one_buffer():
+@pytest.mark.parametrize("m,k", [(37, 640), (512, 8192)])
+def test_halves_of_one_buffer(m, k):
     # gate and up as the two halves of one [m, 2k] gate+up output (row pitch 2k)
     rng = np.random.default_rng(9)
-    m, k = 37, 640
     both = inputs.bf16_normal(rng, m, 2 * k, scale=2.0)
     q_ref, s_ref = oracle.silu_mul_requant(both[:, :k].copy(), both[:, k:].copy())
     d = to_dev(both.view(np.int16))
