@@ -65,6 +65,8 @@ def lib():
         L.orc_block_partials.argtypes = [_i8p, _i8p, _i32p, _i64, _i64, _i64]
         L.orc_gemm_ref.restype = ctypes.c_int
         L.orc_gemm_ref.argtypes = [_i8p, _i8p, _f32p, _f32p, _i64p, _i64, _f64p, _f64p, _i64, _i64]
+        L.orc_w4a16_ref.restype = ctypes.c_int
+        L.orc_w4a16_ref.argtypes = [_u16p, _u8p, _u8p, ctypes.c_float, _i64p, _i64, _f64p, _f64p, _i64, _i64]
         L.orc_max_threads.restype = ctypes.c_int
         L.orc_set_threads.argtypes = [ctypes.c_int]
         _LIB = L
@@ -180,6 +182,26 @@ def gemm_ref(a_i8, w_i8, a_scale, w_scale, rows=None):
     rc = lib().orc_gemm_ref(_ptr(a, _i8p), _ptr(w, _i8p), _ptr(a_s, _f32p), _ptr(w_s, _f32p),
                             _ptr(rows, _i64p), rows.size, _ptr(y, _f64p), _ptr(t, _f64p), n, k)
     _check(rc, "gemm_ref")
+    return y, t
+
+
+def w4a16_ref(x_bf16_bits, w_packed, w_e4m3, scale2, rows=None):
+    """FP64 reference (y, t) of BF16 activations times the dequantized NVFP4 weight."""
+    x = np.ascontiguousarray(x_bf16_bits, dtype=np.uint16)
+    wp = np.ascontiguousarray(w_packed, dtype=np.uint8)
+    we = np.ascontiguousarray(w_e4m3, dtype=np.uint8)
+    m, k = x.shape
+    n = wp.shape[0]
+    if wp.shape != (n, k // 2) or we.shape != (n, k // 16):
+        raise ValueError("weight shapes do not match k")
+    if rows is None:
+        rows = np.arange(m, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    y = np.empty((rows.size, n), np.float64)
+    t = np.empty((rows.size, n), np.float64)
+    rc = lib().orc_w4a16_ref(_ptr(x, _u16p), _ptr(wp, _u8p), _ptr(we, _u8p), float(np.float32(scale2)),
+                             _ptr(rows, _i64p), rows.size, _ptr(y, _f64p), _ptr(t, _f64p), n, k)
+    _check(rc, "w4a16_ref")
     return y, t
 
 

@@ -288,6 +288,47 @@ int orc_gemm_ref(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
     return ORC_OK;
 }
 
+/* ---- f3: W4A16 decode GEMV reference (page "metrale_model_layers/layers/ops/
+ * gemv_sw.rs": BF16 activations times an NVFP4 weight -- packed E2M1, one E4M3
+ * scale per 16, one F32 scale_2 -- with no int8 requant).  The page gives only
+ * the launch; the reading taken: the weight is dequantized exactly as in the
+ * weight requant, e2m1 * s16 * scale2, and
+ *   y[i][j] = sum_k x[i][k] * e2m1[j][k] * s16[j][k/16] * scale2
+ * in FP64, where every term is exact (8 + 2 + 4 + 24 significant bits); t is
+ * the sum of the terms' magnitudes, for the FP32 error bound.
+ * x [m, k] BF16 bits, w_packed [n, k/2], w_e4m3 [n, k/16]; y, t [nrows, n]. */
+int orc_w4a16_ref(const uint16_t *x_bf16, const uint8_t *w_packed, const uint8_t *w_e4m3,
+                  float scale2, const int64_t *rows, int64_t nrows, double *y, double *t,
+                  int64_t n, int64_t k)
+{
+    if (k <= 0 || k % 32 != 0)
+        return ORC_EK;
+    int status = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t j = 0; j < n; ++j) {
+        for (int64_t r = 0; r < nrows; ++r) {
+            const int64_t i = rows[r];
+            double acc = 0.0, mag = 0.0;
+            for (int64_t c = 0; c < k; ++c) {
+                uint8_t byte = w_packed[j * (k / 2) + c / 2];
+                uint32_t code = (c & 1) ? (uint32_t)(byte >> 4) : (uint32_t)(byte & 15u);
+                double w = (double)orc_e2m1_value(code) * (double)orc_e4m3_value(w_e4m3[j * (k / 16) + c / 16]) *
+                           (double)scale2;
+                double term = (double)bf16_to_f32(x_bf16[i * k + c]) * w;
+                acc += term;
+                mag += fabs(term);
+            }
+            if (!isfinite(acc)) {
+#pragma omp atomic write
+                status = ORC_ENONFINITE;
+            }
+            y[r * n + j] = acc;
+            t[r * n + j] = mag;
+        }
+    }
+    return status;
+}
+
 int orc_max_threads(void)
 {
 #ifdef _OPENMP

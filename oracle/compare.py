@@ -12,6 +12,10 @@ Clause (ii) is the first-order worst-case error of an FP32 sum of K/32 rescaled
 block terms taken in any order (one rounding for the scale product, one for the
 product with P, K/32 - 1 for the additions), plus the final BF16 rounding.  It
 only matters under cancellation, where |y| is far below T.
+
+The W4A16 decode GEMV sums K exact per-element terms instead of K/32 block
+terms, adds up to 16 per-wave partial sums and rounds once for scale_2: its
+bound takes `terms` = K + 16 in place of K/32 (T = sum of |x * w|).
 """
 from dataclasses import dataclass
 
@@ -51,8 +55,9 @@ class CheckResult:
                 + (f", first failure at {self.first_failure}" if self.failures else ""))
 
 
-def check_bf16(out_bits, y64, t, k) -> CheckResult:
-    """Apply the pass rule element-wise; out_bits are raw BF16 uint16 values."""
+def check_bf16(out_bits, y64, t, k, terms=None) -> CheckResult:
+    """Apply the pass rule element-wise; out_bits are raw BF16 uint16 values.
+    `terms` is the number of FP32 sum terms of the bound (default K/32)."""
     out = bf16_bits_to_f64(out_bits).reshape(np.shape(y64))
     y = np.asarray(y64, dtype=np.float64)
     t = np.asarray(t, dtype=np.float64)
@@ -61,7 +66,7 @@ def check_bf16(out_bits, y64, t, k) -> CheckResult:
     ay = np.abs(y)
     ulp_y = bf16_ulp(ay)
     ok_i = finite & (err <= np.maximum(4e-3 * ay, ulp_y))
-    bound = (k / 32 + 2) * 2.0 ** -24 * t
+    bound = ((k / 32 if terms is None else terms) + 2) * 2.0 ** -24 * t
     ok_ii = finite & (err <= bound + bf16_ulp(ay + bound))
     ok = ok_i | ok_ii
     nz = ok_i & (ay > 0)
