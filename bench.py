@@ -233,10 +233,22 @@ def main():
             torch.cuda.synchronize()
             t_qv = e0.elapsed_time(e1) * 1e-3 / it
             alg = p.n * p.k * 1.125 + p.m * p.k * 1.125 + 2 * p.m * p.n
+            del copies
+            # W4A16: the same product straight from the NVFP4 weight (0.5625 B per weight)
+            w4bytes = p.n * p.k * (0.5 + 1 / 16)
+            ncopy4 = max(2, int(np.ceil(2 ** 30 / w4bytes)))
+            wp_d, we_d = dev_t(wp), dev_t(we)
+            copies4 = [(wp_d.clone(), we_d.clone()) for _ in range(ncopy4)]
+            out4 = torch.empty((p.m, p.n), dtype=torch.int16, device=dev)
+            t_4 = burst(lambda i: bsr.w4a16_gemv(a_dev, copies4[i % ncopy4][0], copies4[i % ncopy4][1],
+                                                 float(p.scale2), out4, stream=stream), it)
+            alg4 = w4bytes + p.m * p.k * 2 + 2 * p.m * p.n
             dec[p.name] = dict(m=p.m, n=p.n, k=p.k, gemv_us_burst=t_v * 1e6,
                                gemv_gbs=alg / t_v / 1e9, gemv_frac_hbm=alg / t_v / 1e9 / PEAK_HBM_GBS,
-                               requant_a_plus_gemv_us_burst=t_qv * 1e6)
-            del copies
+                               requant_a_plus_gemv_us_burst=t_qv * 1e6,
+                               w4a16_us_burst=t_4 * 1e6, w4a16_gbs=alg4 / t_4 / 1e9,
+                               w4a16_frac_hbm=alg4 / t_4 / 1e9 / PEAK_HBM_GBS)
+            del copies4
             torch.cuda.empty_cache()
         gbs = [d["gemv_gbs"] for d in dec.values()]
         rec["decode"] = dict(cases=dec, gemv_gbs_mean=float(np.mean(gbs)),

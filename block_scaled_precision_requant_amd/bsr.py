@@ -25,6 +25,7 @@ SIGNATURES = {
     "int8_gemm_blockscaled": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u32, _u32, _vp]),
     "int8_gemm_blockscaled_ex": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u32, _u32, _vp, _int]),
     "silu_mul_requant_int8": (_int, [_vp, _vp, _u32, _vp, _vp, _u32, _u32, _vp]),
+    "w4a16_gemv": (_int, [_vp, _vp, _vp, _f32, _vp, _u32, _u32, _u32, _vp]),
     "bsr_status_string": (ctypes.c_char_p, [_int]),
 }
 
@@ -124,6 +125,20 @@ def silu_mul_requant_int8(gate, up, a_i8, a_scale, stream=None):
     st = lib().silu_mul_requant_int8(_ptr(gate), _ptr(up), ld, _ptr(a_i8), _ptr(a_scale), m, k,
                                      _stream(stream, a_i8))
     _done(st, "silu_mul_requant_int8")
+
+
+def w4a16_gemv(x_bf16, w_packed, w_e4m3, scale2, out, stream=None):
+    """out [M,N] BF16 = x_bf16 [M,K] (M <= 8) times the NVFP4 weight (w_packed [N,K/2] u8,
+    w_e4m3 [N,K/16] u8, scale2), dequantized on the fly."""
+    m, k = x_bf16.shape
+    n = w_packed.shape[0]
+    _shape(x_bf16, (m, k), "x_bf16")
+    _shape(w_packed, (n, k // 2), "w_packed")
+    _shape(w_e4m3, (n, k // 16), "w_e4m3")
+    _shape(out, (m, n), "out")
+    st = lib().w4a16_gemv(_ptr(x_bf16), _ptr(w_packed), _ptr(w_e4m3), float(scale2), _ptr(out), m, n, k,
+                          _stream(stream, out))
+    _done(st, "w4a16_gemv")
 
 
 def int8_gemm_blockscaled_ex(a_i8, w_i8, a_scale, w_scale, out, path=PATH_AUTO, stream=None):

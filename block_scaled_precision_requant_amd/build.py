@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsr.so")
-SOURCES = ["requant.hip", "gemm.hip", "gemv.hip", "api.hip"]
+SOURCES = ["requant.hip", "gemm.hip", "gemv.hip", "w4a16.hip", "api.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

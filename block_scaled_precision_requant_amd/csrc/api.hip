@@ -95,6 +95,18 @@ int silu_mul_requant_int8(const uint16_t *gate, const uint16_t *up, uint32_t ld,
     return launched(bsr::launch_silu_requant(gate, up, ld, a_i8, a_scale, m, k, static_cast<hipStream_t>(stream)));
 }
 
+int w4a16_gemv(const uint16_t *x_bf16, const uint8_t *w_packed, const uint8_t *w_e4m3, float scale2,
+               uint16_t *out, uint32_t m, uint32_t n, uint32_t k, void *stream) {
+    if (!k_ok(k) || !std::isfinite(scale2) || m > (uint32_t)bsr::kGemvMaxRows) return BSR_EINVAL;
+    if (m == 0 || n == 0) return BSR_OK;
+    if (!x_bf16 || !w_packed || !w_e4m3 || !out) return BSR_ENULL;
+    if (!aligned(x_bf16, 16) || !aligned(w_packed, 16) || !aligned(out, 2)) return BSR_EALIGN;
+    if (k % 256 == 0 ? !aligned(w_e4m3, 16) : !aligned(w_e4m3, 2)) return BSR_EALIGN;
+    if (bsr::div_up(n, bsr::kGemvCols) > kMaxGrid) return BSR_EINVAL;
+    if (int st = check_device()) return st;
+    return launched(bsr::launch_w4a16(x_bf16, w_packed, w_e4m3, scale2, out, m, n, k, static_cast<hipStream_t>(stream)));
+}
+
 int int8_gemm_blockscaled_ex(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
                              const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                              void *stream, int path) {

@@ -51,6 +51,11 @@ constexpr int kGemvMaxWaves = 16;
 constexpr int kGemvMaxRows = 8;
 constexpr int kGemvBlocksPerIter = 4;   // K blocks per loop iteration of a wave (two MFMA steps)
 
+// ---- W4A16 decode GEMV (m <= 8, straight from NVFP4) ------------------------
+// Same workgroup shape as the int8 GEMV; K in super-steps of 128, at most
+// kW4PassSteps per staging pass of a wave.
+constexpr int kW4PassSteps = 8;
+
 inline uint64_t div_up(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
 // Launchers (no validation: the C-ABI layer has checked every argument).
@@ -60,6 +65,8 @@ hipError_t launch_requant_a(const uint16_t *a_bf16, int8_t *a_i8, float *a_scale
                             uint64_t nblocks, hipStream_t s);
 hipError_t launch_silu_requant(const uint16_t *gate, const uint16_t *up, uint32_t ld, int8_t *a_i8,
                                float *a_scale, uint32_t m, uint32_t k, hipStream_t s);
+hipError_t launch_w4a16(const uint16_t *x, const uint8_t *w_packed, const uint8_t *w_e4m3, float scale2,
+                        uint16_t *out, uint32_t m, uint32_t n, uint32_t k, hipStream_t s);
 hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
                        const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
                        uint32_t k, hipStream_t s);

@@ -146,6 +146,24 @@ int int8_gemm_blockscaled_ex(const int8_t *a_i8, const int8_t *w_i8, const float
 int silu_mul_requant_int8(const uint16_t *gate, const uint16_t *up, uint32_t ld, int8_t *a_i8,
                           float *a_scale, uint32_t m, uint32_t k, void *stream);
 
+/*
+ * W4A16 decode GEMV straight from the NVFP4 weight, no int8 requant (the
+ * decode launcher of page "metrale_model_layers/layers/ops/gemv_sw.rs":
+ * BF16 input, packed weight, E4M3 weight scale, F32 scale_2, BF16 output).
+ *   x_bf16   [m, k]    BF16 as raw u16, 16-byte aligned, 1 <= m <= 8
+ *   w_packed [n, k/2]  u8 (E2M1 pairs, low nibble first), 16-byte aligned
+ *   w_e4m3   [n, k/16] u8, 16-byte aligned when k % 256 == 0, else 2-byte
+ *   out      [m, n]    BF16 as raw u16, 2-byte aligned
+ * out[i,j] = bf16_rne( fl32( S * scale2 ) ), S = FP32 sum over k of
+ * x[i,k] * e2m1[j,k] * s16[j,k/16] (each product exact; the summation order
+ * is the kernel's own): within 4e-3 relative or 1 BF16 ulp of the FP64 value,
+ * or within the worst-case FP32 error of a (k + 16)-term sum.
+ * Errors: BSR_EINVAL (k, m > 8, scale2 not finite), BSR_ENULL, BSR_EALIGN,
+ * BSR_EDEVICE, BSR_ELAUNCH.
+ */
+int w4a16_gemv(const uint16_t *x_bf16, const uint8_t *w_packed, const uint8_t *w_e4m3, float scale2,
+               uint16_t *out, uint32_t m, uint32_t n, uint32_t k, void *stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *bsr_status_string(int status);
 

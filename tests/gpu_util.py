@@ -65,3 +65,12 @@ def gpu_silu_requant(gate_bits, up_bits):
     s = torch.empty((m, k // 32), dtype=torch.float32, device=DEV)
     bsr.silu_mul_requant_int8(g, u, q, s)
     return q, s
+
+
+def gpu_w4a16(x_bits, packed, e4m3, scale2):
+    x = to_dev(x_bits.view(np.int16))
+    wp, we = to_dev(packed), to_dev(e4m3)
+    m, n = x.shape[0], wp.shape[0]
+    out = torch.empty((m, n), dtype=torch.int16, device=DEV)
+    bsr.w4a16_gemv(x, wp, we, float(scale2), out)
+    return out

@@ -89,6 +89,18 @@ def test_silu_requant_validation():
     assert L.silu_mul_requant_int8(FAKE, FAKE, 64, FAKE, _fake(2), 4, 64, None) == bsr.BSR_EALIGN
 
 
+def test_w4a16_validation():
+    L = bsr.lib()
+    null = ctypes.c_void_p(0)
+    assert L.w4a16_gemv(FAKE, FAKE, FAKE, 1.0, FAKE, 9, 4, 256, None) == bsr.BSR_EINVAL    # m > 8
+    assert L.w4a16_gemv(FAKE, FAKE, FAKE, 1.0, FAKE, 1, 4, 48, None) == bsr.BSR_EINVAL     # k
+    assert L.w4a16_gemv(FAKE, FAKE, FAKE, float("nan"), FAKE, 1, 4, 256, None) == bsr.BSR_EINVAL
+    assert L.w4a16_gemv(FAKE, FAKE, FAKE, 1.0, FAKE, 0, 4, 256, None) == bsr.BSR_OK
+    assert L.w4a16_gemv(null, FAKE, FAKE, 1.0, FAKE, 1, 4, 256, None) == bsr.BSR_ENULL
+    assert L.w4a16_gemv(FAKE, FAKE, _fake(2), 1.0, FAKE, 1, 4, 256, None) == bsr.BSR_EALIGN  # k % 256 == 0
+    assert L.w4a16_gemv(FAKE, _fake(8), FAKE, 1.0, FAKE, 1, 4, 96, None) == bsr.BSR_EALIGN
+
+
 def test_bad_scale2_and_path():
     L = bsr.lib()
     for s2 in (float("nan"), float("inf"), -float("inf")):
