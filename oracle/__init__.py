@@ -65,6 +65,12 @@ def lib():
         L.orc_block_partials.argtypes = [_i8p, _i8p, _i32p, _i64, _i64, _i64]
         L.orc_gemm_ref.restype = ctypes.c_int
         L.orc_gemm_ref.argtypes = [_i8p, _i8p, _f32p, _f32p, _i64p, _i64, _f64p, _f64p, _i64, _i64]
+        L.orc_e4m3_encode.restype = ctypes.c_uint32
+        L.orc_e4m3_encode.argtypes = [ctypes.c_float]
+        L.orc_quant_act.restype = ctypes.c_int
+        L.orc_quant_act.argtypes = [_u16p, _u8p, _f32p, _i64, _i64, _i64, ctypes.c_int]
+        L.orc_gemm_ref_agroup.restype = ctypes.c_int
+        L.orc_gemm_ref_agroup.argtypes = [_i8p, _i8p, _f32p, _f32p, _i64p, _i64, _f64p, _f64p, _i64, _i64, _i64]
         L.orc_w4a16_ref.restype = ctypes.c_int
         L.orc_w4a16_ref.argtypes = [_u16p, _u8p, _u8p, ctypes.c_float, _i64p, _i64, _f64p, _f64p, _i64, _i64]
         L.orc_max_threads.restype = ctypes.c_int
@@ -182,6 +188,42 @@ def gemm_ref(a_i8, w_i8, a_scale, w_scale, rows=None):
     rc = lib().orc_gemm_ref(_ptr(a, _i8p), _ptr(w, _i8p), _ptr(a_s, _f32p), _ptr(w_s, _f32p),
                             _ptr(rows, _i64p), rows.size, _ptr(y, _f64p), _ptr(t, _f64p), n, k)
     _check(rc, "gemm_ref")
+    return y, t
+
+
+def e4m3_encode(x: float) -> int:
+    """Nearest OCP E4M3 code of a binary32 (ties to even, saturating at 448)."""
+    return int(lib().orc_e4m3_encode(float(np.float32(x))))
+
+
+def quant_act(a_bf16_bits, group, e4m3=False):
+    """BF16 activations -> (codes [M,K] uint8 (int8 or E4M3 bytes), scales [M,K/group] float32);
+    group 32, 128 or K (one scale per row)."""
+    a = np.ascontiguousarray(a_bf16_bits, dtype=np.uint16)
+    m, k = a.shape
+    q = np.empty((m, k), np.uint8)
+    s = np.empty((m, max(k // group, 0)), np.float32)
+    rc = lib().orc_quant_act(_ptr(a, _u16p), _ptr(q, _u8p), _ptr(s, _f32p), m, k, group, int(bool(e4m3)))
+    _check(rc, "quant_act")
+    return q, s
+
+
+def gemm_ref_agroup(a_i8, w_i8, a_scale, w_scale, group, rows=None):
+    """FP64 reference (y, t) with activation scales per `group` (32, 128 or K) and per-32 weight scales."""
+    a = np.ascontiguousarray(a_i8, dtype=np.int8)
+    w = np.ascontiguousarray(w_i8, dtype=np.int8)
+    a_s = np.ascontiguousarray(a_scale, dtype=np.float32)
+    w_s = np.ascontiguousarray(w_scale, dtype=np.float32)
+    m, k = a.shape
+    n = w.shape[0]
+    if rows is None:
+        rows = np.arange(m, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    y = np.empty((rows.size, n), np.float64)
+    t = np.empty((rows.size, n), np.float64)
+    rc = lib().orc_gemm_ref_agroup(_ptr(a, _i8p), _ptr(w, _i8p), _ptr(a_s, _f32p), _ptr(w_s, _f32p),
+                                   _ptr(rows, _i64p), rows.size, _ptr(y, _f64p), _ptr(t, _f64p), n, k, group)
+    _check(rc, "gemm_ref_agroup")
     return y, t
 
 

@@ -36,6 +36,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -236,6 +237,134 @@ int orc_silu_mul_requant(const uint16_t *gate, const uint16_t *up, int64_t ld, i
         }
     }
     return status;
+}
+
+/* ---- f4: other activation scale layouts and E4M3 activations. -----------
+ * The W8A8 parts of page "metrale_model_layers/layers/ops/w8a8_decode/parts.rs"
+ * (`W8a8Scale::PerRow`, `W8a8Scale::Block128`, the `[rows, k]` E4M3 activation
+ * with its FP32 scales) and the per-(row, 128) E4M3 quantizer of page
+ * ".../fp8_moe_grouped_tc_w8a8.rs" fix the layouts but not the arithmetic.
+ * Reading taken: the per-32 rule above with the group size G (32, 128 or the
+ * whole row) and, for E4M3, the format's largest finite value in place of 127:
+ *   int8: s = fl32(amax / 127), q = clamp(rne(fl32(v / s)), -127, 127);
+ *   E4M3: s = fl32(amax / 448), q = the OCP E4M3 code nearest fl32(v / s),
+ *         ties to the even code, magnitudes above 448 saturating to 448;
+ * s == 0 gives +0.0f and code 0 in both. */
+
+/* Nearest OCP E4M3 code of a binary32 (ties to even, saturating at 448). */
+uint32_t orc_e4m3_encode(float x)
+{
+    uint32_t sign = signbit(x) ? 0x80u : 0u;
+    double a = fabs((double)x);
+    if (a >= 448.0)
+        return sign | 0x7Eu;
+    if (a == 0.0)
+        return sign;
+    /* the finite E4M3 magnitudes: subnormals m * 2^-9 (m < 8), normals
+     * (8 + m) * 2^(e - 10) for e = 1..15, m = 0..7 (excluding the NaN code) */
+    int e;
+    frexp(a, &e);                 /* a = f * 2^e, 0.5 <= f < 1 */
+    int ex = e - 1 + 7;           /* biased exponent if a is normal */
+    double unit = ex >= 1 ? ldexp(1.0, e - 1 - 3) : ldexp(1.0, -9);
+    double n = nearbyint(a / unit); /* exact quotient (power-of-two unit), ties to even */
+    uint32_t code;
+    if (ex >= 1) {
+        /* n in [8, 16]; 16 means the next binade's 8 */
+        code = n >= 16.0 ? (uint32_t)((ex + 1) << 3) : (uint32_t)((ex << 3) | ((uint32_t)n - 8u));
+    } else {
+        code = (uint32_t)n; /* 8 is the smallest normal, code 0x08 */
+    }
+    if (code > 0x7Eu)
+        code = 0x7Eu;
+    return sign | code;
+}
+
+static int quantize_group(const float *v, int64_t g, int e4m3, uint8_t *q, float *scale)
+{
+    float amax = 0.0f;
+    for (int64_t i = 0; i < g; ++i) {
+        if (!isfinite(v[i]))
+            return ORC_ENONFINITE;
+        float a = fabsf(v[i]);
+        if (a > amax)
+            amax = a;
+    }
+    float s = amax / (e4m3 ? 448.0f : 127.0f);
+    if (s == 0.0f) {
+        *scale = 0.0f;
+        memset(q, 0, (size_t)g);
+        return ORC_OK;
+    }
+    *scale = s;
+    for (int64_t i = 0; i < g; ++i) {
+        float r = v[i] / s;
+        if (e4m3) {
+            q[i] = (uint8_t)orc_e4m3_encode(r);
+        } else {
+            float t = nearbyintf(r);
+            if (t > 127.0f)
+                t = 127.0f;
+            if (t < -127.0f)
+                t = -127.0f;
+            q[i] = (uint8_t)(int8_t)t;
+        }
+    }
+    return ORC_OK;
+}
+
+/* a_bf16 [m, k] -> q [m, k] (int8 or E4M3 codes as bytes), scale [m, k / g];
+ * group g = 32, 128 or k (one scale per row); g must divide k. */
+int orc_quant_act(const uint16_t *a_bf16, uint8_t *q, float *scale, int64_t m, int64_t k,
+                  int64_t g, int e4m3)
+{
+    if (k <= 0 || k % 32 != 0 || g <= 0 || k % g != 0)
+        return ORC_EK;
+    int status = ORC_OK;
+    const int64_t ng = k / g;
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < m; ++row) {
+        float *v = (float *)malloc((size_t)g * sizeof(float));
+        for (int64_t b = 0; b < ng; ++b) {
+            for (int64_t j = 0; j < g; ++j)
+                v[j] = bf16_to_f32(a_bf16[row * k + g * b + j]);
+            int rc = quantize_group(v, g, e4m3, q + row * k + g * b, scale + row * ng + b);
+            if (rc != ORC_OK) {
+#pragma omp atomic write
+                status = rc;
+            }
+        }
+        free(v);
+    }
+    return status;
+}
+
+/* Reference of the int8 GEMM with activation scales per group of g (32, 128
+ * or k): term = a_scale[i][32 b / g] * w_scale[j][b] * P[i, j, b]. */
+int orc_gemm_ref_agroup(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
+                        const float *w_scale, const int64_t *rows, int64_t nrows,
+                        double *y, double *t, int64_t n, int64_t k, int64_t g)
+{
+    if (k <= 0 || k % 32 != 0 || g <= 0 || g % 32 != 0 || k % g != 0)
+        return ORC_EK;
+    const int64_t nb = k / 32, ng = k / g;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = rows[r];
+        for (int64_t j = 0; j < n; ++j) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t b = 0; b < nb; ++b) {
+                int32_t p = 0;
+                for (int u = 0; u < 32; ++u)
+                    p += (int32_t)a_i8[i * k + 32 * b + u] * (int32_t)w_i8[j * k + 32 * b + u];
+                double term = (double)a_scale[i * ng + (32 * b) / g] * (double)w_scale[j * nb + b] * (double)p;
+                acc += term;
+                mag += fabs(term);
+            }
+            y[r * n + j] = acc;
+            t[r * n + j] = mag;
+        }
+    }
+    return ORC_OK;
 }
 
 /* ---- O5: exact int32 block partials P[m, n, k/32]. --------------------- */
