@@ -26,6 +26,8 @@ SIGNATURES = {
     "int8_gemm_blockscaled_ex": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u32, _u32, _vp, _int]),
     "silu_mul_requant_int8": (_int, [_vp, _vp, _u32, _vp, _vp, _u32, _u32, _vp]),
     "w4a16_gemv": (_int, [_vp, _vp, _vp, _f32, _vp, _u32, _u32, _u32, _vp]),
+    "quantize_act": (_int, [_vp, _vp, _vp, _u32, _u32, _u32, _int, _vp]),
+    "int8_gemm_blockscaled_agroup": (_int, [_vp, _vp, _vp, _u32, _vp, _vp, _u32, _u32, _u32, _vp, _int]),
     "bsr_status_string": (ctypes.c_char_p, [_int]),
 }
 
@@ -167,6 +169,39 @@ def int8_gemm_blockscaled(a_i8, w_i8, a_scale, w_scale, out, stream=None):
     st = lib().int8_gemm_blockscaled(_ptr(a_i8), _ptr(w_i8), _ptr(a_scale), _ptr(w_scale), _ptr(out),
                                      m, n, k, _stream(stream, out))
     _done(st, "int8_gemm_blockscaled")
+
+
+FMT_INT8, FMT_E4M3 = 0, 1
+
+
+def _scale_cols(k, group):
+    return 1 if group == 0 else k // group
+
+
+def quantize_act(a_bf16, q, scale, group=32, fmt=FMT_INT8, stream=None):
+    """BF16 a_bf16 [M,K] -> codes q [M,K] (uint8: int8 or E4M3 bits) and float32
+    scales [M, K/group] (group 32 or 128) or [M, 1] (group 0: one per row)."""
+    m, k = a_bf16.shape
+    _shape(a_bf16, (m, k), "a_bf16")
+    _shape(q, (m, k), "q")
+    _shape(scale, (m, _scale_cols(k, group)), "scale")
+    st = lib().quantize_act(_ptr(a_bf16), _ptr(q), _ptr(scale), m, k, int(group), int(fmt), _stream(stream, q))
+    _done(st, "quantize_act")
+
+
+def int8_gemm_blockscaled_agroup(a_i8, w_i8, a_scale, a_group, w_scale, out, path=PATH_AUTO, stream=None):
+    """int8_gemm_blockscaled_ex with activation scales a_scale [M, K/a_group]
+    (a_group 32 or 128) or [M, 1] (a_group 0: one per row)."""
+    m, k = a_i8.shape
+    n = w_i8.shape[0]
+    _shape(a_i8, (m, k), "a_i8")
+    _shape(w_i8, (n, k), "w_i8")
+    _shape(a_scale, (m, _scale_cols(k, a_group)), "a_scale")
+    _shape(w_scale, (n, k // 32), "w_scale")
+    _shape(out, (m, n), "out")
+    st = lib().int8_gemm_blockscaled_agroup(_ptr(a_i8), _ptr(w_i8), _ptr(a_scale), int(a_group), _ptr(w_scale),
+                                            _ptr(out), m, n, k, _stream(stream, out), int(path))
+    _done(st, "int8_gemm_blockscaled_agroup")
 
 
 def prefill(a_bf16, w_i8, w_scale, a_i8_scratch, a_scale_scratch, out, stream=None):

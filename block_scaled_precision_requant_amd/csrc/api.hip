@@ -107,22 +107,59 @@ int w4a16_gemv(const uint16_t *x_bf16, const uint8_t *w_packed, const uint8_t *w
     return launched(bsr::launch_w4a16(x_bf16, w_packed, w_e4m3, scale2, out, m, n, k, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+int gemm_launch(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
+                uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                void *stream, int path) {
+    if (int st = check_device()) return st;
+    const bool gemv = path == BSR_PATH_GEMV || (path == BSR_PATH_AUTO && m <= (uint32_t)bsr::kGemvMaxRows);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (gemv) return launched(bsr::launch_gemv(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s));
+    return launched(bsr::launch_gemm(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s));
+}
+
+}  // namespace
+
 int int8_gemm_blockscaled_ex(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
                              const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                              void *stream, int path) {
     if (int st = gemm_args_check(a_i8, w_i8, a_scale, w_scale, out, m, n, k, path)) return st;
     if (m == 0 || n == 0) return BSR_OK;
-    if (int st = check_device()) return st;
-    const bool gemv = path == BSR_PATH_GEMV || (path == BSR_PATH_AUTO && m <= (uint32_t)bsr::kGemvMaxRows);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (gemv) return launched(bsr::launch_gemv(a_i8, w_i8, a_scale, w_scale, out, m, n, k, s));
-    return launched(bsr::launch_gemm(a_i8, w_i8, a_scale, w_scale, out, m, n, k, s));
+    return gemm_launch(a_i8, w_i8, a_scale, k / 32, 0, w_scale, out, m, n, k, stream, path);
 }
 
 int int8_gemm_blockscaled(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
                           const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                           void *stream) {
     return int8_gemm_blockscaled_ex(a_i8, w_i8, a_scale, w_scale, out, m, n, k, stream, BSR_PATH_AUTO);
+}
+
+int int8_gemm_blockscaled_agroup(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
+                                 uint32_t a_group, const float *w_scale, uint16_t *out, uint32_t m,
+                                 uint32_t n, uint32_t k, void *stream, int path) {
+    if (a_group != 0 && a_group != 32 && a_group != 128) return BSR_EINVAL;
+    if (a_group == 128 && k % 128 != 0) return BSR_EINVAL;
+    if (int st = gemm_args_check(a_i8, w_i8, a_scale, w_scale, out, m, n, k, path)) return st;
+    if (m == 0 || n == 0) return BSR_OK;
+    const uint32_t a_ld = a_group == 0 ? 1 : k / a_group;
+    const uint32_t a_shift = a_group == 0 ? 31 : (a_group == 128 ? 2 : 0);
+    return gemm_launch(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, stream, path);
+}
+
+int quantize_act(const uint16_t *a_bf16, uint8_t *q, float *scale, uint32_t m, uint32_t k,
+                 uint32_t group, int format, void *stream) {
+    if (!k_ok(k) || (group != 0 && group != 32 && group != 128)) return BSR_EINVAL;
+    if (group == 128 && k % 128 != 0) return BSR_EINVAL;
+    if (format != BSR_FMT_INT8 && format != BSR_FMT_E4M3) return BSR_EINVAL;
+    if (m == 0) return BSR_OK;
+    if (!a_bf16 || !q || !scale) return BSR_ENULL;
+    if (!aligned(a_bf16, 16) || !aligned(q, 8) || !aligned(scale, 4)) return BSR_EALIGN;
+    const uint64_t nchunks = (uint64_t)m * (k / 8);
+    if (m > kMaxGrid || bsr::div_up(nchunks, bsr::kRqaThreads) > kMaxGrid) return BSR_EINVAL;
+    if (int st = check_device()) return st;
+    return launched(bsr::launch_quant_act(a_bf16, q, scale, m, k, group, format == BSR_FMT_E4M3,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 const char *bsr_status_string(int status) {

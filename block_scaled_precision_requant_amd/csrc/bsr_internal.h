@@ -67,11 +67,15 @@ hipError_t launch_silu_requant(const uint16_t *gate, const uint16_t *up, uint32_
                                float *a_scale, uint32_t m, uint32_t k, hipStream_t s);
 hipError_t launch_w4a16(const uint16_t *x, const uint8_t *w_packed, const uint8_t *w_e4m3, float scale2,
                         uint16_t *out, uint32_t m, uint32_t n, uint32_t k, hipStream_t s);
-hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
-                       const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
+hipError_t launch_quant_act(const uint16_t *a_bf16, uint8_t *q, float *scale, uint32_t m, uint32_t k,
+                            uint32_t group, bool e4m3, hipStream_t s);
+// a_scale row r, block b: a_scale[r * a_ld + (b >> a_shift)] (a_ld = k / 32 and
+// a_shift = 0 for one activation scale per block).
+hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
+                       uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
                        uint32_t k, hipStream_t s);
-hipError_t launch_gemv(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
-                       const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
+hipError_t launch_gemv(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
+                       uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
                        uint32_t k, hipStream_t s);
 
 }  // namespace bsr

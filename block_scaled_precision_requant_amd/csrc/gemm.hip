@@ -108,10 +108,13 @@ __device__ __forceinline__ void copy_rows(int8_t *dst, const int8_t *src, uint32
 }
 
 // One scale tile's copies: NSEGS segments of 64 floats, consecutive lanes on
-// the (swizzled) blocks of a row.
+// the (swizzled) blocks of a row.  Block b of row r reads src[r * ld + (b >>
+// shift)]: ld = nb, shift = 0 for a scale per block; an activation scale per
+// 128 elements has ld = nb / 4, shift = 2, one per row ld = 1, shift = 31.
 template <int NSEGS, int NWAVES>
 __device__ __forceinline__ void copy_scales(float *dst, const float *src, uint32_t rows_limit,
-                                            uint32_t r0, uint32_t nb, uint32_t kb, int wave, int lane) {
+                                            uint32_t r0, uint32_t ld, uint32_t shift, uint32_t nb,
+                                            uint32_t kb, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < (NSEGS + NWAVES - 1) / NWAVES; ++i) {
         const int seg = wave + i * NWAVES;
@@ -119,7 +122,7 @@ __device__ __forceinline__ void copy_scales(float *dst, const float *src, uint32
         const uint32_t idx = seg * 64 + lane;  // = row * kGemmStageBlocks + slot
         const uint32_t row = idx / kGemmStageBlocks;
         const uint32_t blk = min(kb + ((idx % kGemmStageBlocks) ^ scale_swz(row)), nb - 1);
-        __builtin_amdgcn_global_load_lds(src + (uint64_t)min(r0 + row, rows_limit - 1) * nb + blk,
+        __builtin_amdgcn_global_load_lds(src + (uint64_t)min(r0 + row, rows_limit - 1) * ld + (blk >> shift),
                                          (lds_void *)(dst + seg * 64), 4, 0, 0);
     }
 }
@@ -127,12 +130,13 @@ __device__ __forceinline__ void copy_scales(float *dst, const float *src, uint32
 template <class G, int BM, int BN>
 __device__ __forceinline__ void issue_stage(Stage<BM, BN> &st, const int8_t *a, const int8_t *w,
                                             const float *a_s, const float *w_s, uint32_t M,
-                                            uint32_t N, uint32_t K, uint32_t nb, uint32_t m0,
-                                            uint32_t n0, uint32_t kb, int wave, int lane) {
+                                            uint32_t N, uint32_t K, uint32_t nb, uint32_t a_ld,
+                                            uint32_t a_shift, uint32_t m0, uint32_t n0, uint32_t kb,
+                                            int wave, int lane) {
     copy_rows<BM / kRowsPerCopy, G::kWaves>(st.a, a, M, m0, K, kb, wave, lane);
     copy_rows<BN / kRowsPerCopy, G::kWaves>(st.w, w, N, n0, K, kb, wave, lane);
-    copy_scales<BM * kGemmStageBlocks / 64, G::kWaves>(&st.as[0][0], a_s, M, m0, nb, kb, wave, lane);
-    copy_scales<BN * kGemmStageBlocks / 64, G::kWaves>(&st.ws[0][0], w_s, N, n0, nb, kb, wave, lane);
+    copy_scales<BM * kGemmStageBlocks / 64, G::kWaves>(&st.as[0][0], a_s, M, m0, a_ld, a_shift, nb, kb, wave, lane);
+    copy_scales<BN * kGemmStageBlocks / 64, G::kWaves>(&st.ws[0][0], w_s, N, n0, nb, 0, nb, kb, wave, lane);
 }
 
 // Wait until at most n of this wave's global -> LDS copies are outstanding.
@@ -165,7 +169,7 @@ template <int BM, int BN, int WM, int WN, int WG_PER_CU>
 __global__ __launch_bounds__(BM * BN / (WM * WN) * 64, WG_PER_CU) void gemm_kernel(
     const int8_t *__restrict__ a, const int8_t *__restrict__ w, const float *__restrict__ a_s,
     const float *__restrict__ w_s, uint16_t *__restrict__ out, uint32_t M, uint32_t N, uint32_t K,
-    uint32_t tiles_m, uint32_t tiles_n) {
+    uint32_t a_ld, uint32_t a_shift, uint32_t tiles_m, uint32_t tiles_n) {
     using G = Geo<BM, BN, WM, WN>;
     constexpr int TM = G::kTM, TN = G::kTN;
     using St = Stage<BM, BN>;
@@ -267,7 +271,8 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64, WG_PER_CU) void gemm_kern
             for (int j = 0; j < TN; ++j) BSR_PIN16(acc[i][j]);
     };
     auto issue = [&](St &buf, uint32_t stage) {
-        issue_stage<G>(buf, a, w, a_s, w_s, M, N, K, nb, m0, n0, stage * kGemmStageBlocks, wave, lane);
+        issue_stage<G>(buf, a, w, a_s, w_s, M, N, K, nb, a_ld, a_shift, m0, n0, stage * kGemmStageBlocks, wave,
+                       lane);
     };
     // Stage s lives in buffer s % 2.  At the top of stage s each wave waits for
     // its own copies of stage s, the barrier publishes every wave's copies and
@@ -304,31 +309,34 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64, WG_PER_CU) void gemm_kern
 template <int BM, int BN, int WM, int WN, int WG_PER_CU>
 hipError_t launch_tiles(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
                         const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
-                        hipStream_t s) {
+                        uint32_t a_ld, uint32_t a_shift, hipStream_t s) {
     const uint32_t tiles_m = (uint32_t)div_up(m, BM);
     const uint32_t tiles_n = (uint32_t)div_up(n, BN);
     hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, WG_PER_CU>), dim3(tiles_m * tiles_n),
                        dim3(Geo<BM, BN, WM, WN>::kThreads), 0, s, a_i8, w_i8, a_scale, w_scale, out, m, n,
-                       k, tiles_m, tiles_n);
+                       k, a_ld, a_shift, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
-                       const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
-                       hipStream_t s) {
+hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
+                       uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
+                       uint32_t k, hipStream_t s) {
     // m <= 128: one tile row; sixteen 32x32 waves per 128x128 tile keep four
     // waves on every SIMD although the grid is small.
     if (m <= (uint32_t)kGemmBMSmall)
-        return launch_tiles<kGemmBMSmall, kGemmBN, 32, 32, 1>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, s);
+        return launch_tiles<kGemmBMSmall, kGemmBN, 32, 32, 1>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, a_ld,
+                                                              a_shift, s);
     // Up to two rounds of 256x128 tiles over the CUs: one 8-wave workgroup per
     // CU.  Larger grids: two 4-wave 128x128 workgroups per CU, whose barriers
     // fall at different times, so one computes while the other waits.
     const uint64_t big_tiles = div_up(m, kGemmBMLarge) * div_up(n, kGemmBN);
     if (big_tiles <= 2 * (uint64_t)kGemmCus)
-        return launch_tiles<kGemmBMLarge, kGemmBN, 64, 64, 1>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, s);
-    return launch_tiles<kGemmBMSmall, kGemmBN, 64, 64, 2>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, s);
+        return launch_tiles<kGemmBMLarge, kGemmBN, 64, 64, 1>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, a_ld,
+                                                              a_shift, s);
+    return launch_tiles<kGemmBMSmall, kGemmBN, 64, 64, 2>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, a_ld,
+                                                          a_shift, s);
 }
 
 }  // namespace bsr

@@ -110,11 +110,21 @@ __device__ __forceinline__ v4f load_f4(const float *p, uint32_t idx, uint32_t nb
     return r;
 }
 
-template <bool VEC>
+// Activation scales of blocks idx..idx+3 of one row with a scale per 2^shift
+// blocks (shift >= 2): idx is a multiple of 4, so one scale covers all four.
+__device__ __forceinline__ v4f load_group_f4(const float *p, uint32_t idx, uint32_t nb, uint32_t shift) {
+    const float v = p[min(idx, nb - 1) >> shift];
+    const v4f r = {v, v, v, v};
+    return r;
+}
+
+// VEC: 16-byte scale loads (nb % 4 == 0).  AGROUP: activation scales per 2^a_shift
+// blocks (a_shift >= 2), rows a_ld floats apart; else one per block, a_ld = nb.
+template <bool VEC, bool AGROUP>
 __global__ __launch_bounds__(kGemvMaxWaves * 64) void gemv_direct_kernel(
     const int8_t *__restrict__ a, const int8_t *__restrict__ w, const float *__restrict__ a_s,
     const float *__restrict__ w_s, uint16_t *__restrict__ out, uint32_t m, uint32_t n, uint32_t k,
-    uint32_t blocks_per_wave) {
+    uint32_t a_ld, uint32_t a_shift, uint32_t blocks_per_wave) {
     __shared__ float red[kGemvMaxWaves * 64 * 4];
 
     const int lane = threadIdx.x & 63;
@@ -148,8 +158,10 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void gemv_direct_kernel(
         for (int h = 0; h < kQuads; ++h) {
             x.wsv[h] = load_f4<VEC>(wsrow, b0 + 4 * h, nb);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                x.asv[h][r] = load_f4<VEC>(a_s + (uint64_t)min(srow0 + r, m - 1) * nb, b0 + 4 * h, nb);
+            for (int r = 0; r < 4; ++r) {
+                const float *ar = a_s + (uint64_t)min(srow0 + r, m - 1) * a_ld;
+                x.asv[h][r] = AGROUP ? load_group_f4(ar, b0 + 4 * h, nb, a_shift) : load_f4<VEC>(ar, b0 + 4 * h, nb);
+            }
         }
         gemv_iter(acc, x, b0, b_end, a_live, q);
     }
@@ -189,7 +201,7 @@ constexpr int kStagedMaxIters = 8;                   // iterations per wave (unr
 __global__ __launch_bounds__(kGemvMaxWaves * 64) void gemv_staged_kernel(
     const int8_t *__restrict__ a, const int8_t *w, const float *__restrict__ a_s,
     const float *__restrict__ w_s, uint16_t *__restrict__ out, uint32_t m, uint32_t n, uint32_t k,
-    uint32_t bpw) {
+    uint32_t a_ld, uint32_t a_shift, uint32_t bpw) {
     extern __shared__ __attribute__((aligned(1024))) int8_t smem[];
 
     const int lane = threadIdx.x & 63;
@@ -232,15 +244,25 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void gemv_staged_kernel(
                                              (lds_void *)(la + p0), 16, 0, 0);
     }
     // Scale slices: m rows of a_s then 16 rows of w_s, len floats each, in
-    // 16-byte copies (b_begin and len are multiples of 4 and so is nb).
+    // 16-byte copies (b_begin and len are multiples of 4 and so is nb).  With
+    // a_shift > 0 the activation rows are expanded to one scale per block by
+    // 4-byte copies, so the K loop reads the same layout either way.
     const uint32_t s_floats = (m + kGemvCols) * g.s_pitch;
-    for (uint32_t p0 = 0; p0 < s_floats; p0 += 256) {
+    const uint32_t as_floats = a_shift ? m * g.s_pitch : 0;
+    for (uint32_t p0 = as_floats & ~255u; p0 < s_floats; p0 += 256) {
         const uint32_t p = p0 + 4 * lane;
         const uint32_t r = min(p / g.s_pitch, m + kGemvCols - 1), c = min(p % g.s_pitch, len - 4);
-        const float *src = r < m ? a_s + (uint64_t)r * nb
+        const float *src = r < m ? a_s + (uint64_t)r * a_ld
                                  : w_s + (uint64_t)min(n0 + (r - m), n - 1) * nb;
-        if (p < s_floats)
+        if (p < s_floats && p >= as_floats)
             __builtin_amdgcn_global_load_lds(src + b_begin + c, (lds_void *)(ls + p0), 16, 0, 0);
+    }
+    for (uint32_t p0 = 0; p0 < as_floats; p0 += 64) {
+        const uint32_t p = p0 + lane;
+        const uint32_t r = min(p / g.s_pitch, m - 1), c = min(p % g.s_pitch, len - 1);
+        if (p < as_floats)
+            __builtin_amdgcn_global_load_lds(a_s + (uint64_t)r * a_ld + ((b_begin + c) >> a_shift),
+                                             (lds_void *)(ls + p0), 4, 0, 0);
     }
     wait_vm_le<0>();
 
@@ -287,9 +309,9 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void gemv_staged_kernel(
 
 }  // namespace
 
-hipError_t launch_gemv(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
-                       const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
-                       hipStream_t s) {
+hipError_t launch_gemv(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
+                       uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
+                       uint32_t k, hipStream_t s) {
     // Waves per workgroup: enough that the whole launch has ~24 waves per CU
     // (6144 waves over 256 CUs), but at least one iteration per wave.  The
     // staged kernel also needs at most kStagedMaxIters iterations per wave.
@@ -308,16 +330,20 @@ hipError_t launch_gemv(const int8_t *a_i8, const int8_t *w_i8, const float *a_sc
         const uint32_t lds = max(staged_geo(m, bpw).wave_bytes * waves, kRedBytes);
         if (lds <= kLdsBytes) {
             hipLaunchKernelGGL(gemv_staged_kernel, dim3(tiles), dim3(64 * waves), lds, s, a_i8, w_i8,
-                               a_scale, w_scale, out, m, n, k, bpw);
+                               a_scale, w_scale, out, m, n, k, a_ld, a_shift, bpw);
             return hipGetLastError();
         }
     }
-    if (nb % 4 == 0)
-        hipLaunchKernelGGL(gemv_direct_kernel<true>, dim3(tiles), dim3(64 * waves), 0, s, a_i8, w_i8,
-                           a_scale, w_scale, out, m, n, k, bpw);
+    const dim3 grid(tiles), blk(64 * waves);
+    if (a_shift)
+        hipLaunchKernelGGL((gemv_direct_kernel<false, true>), grid, blk, 0, s, a_i8, w_i8, a_scale, w_scale,
+                           out, m, n, k, a_ld, a_shift, bpw);
+    else if (nb % 4 == 0)
+        hipLaunchKernelGGL((gemv_direct_kernel<true, false>), grid, blk, 0, s, a_i8, w_i8, a_scale, w_scale,
+                           out, m, n, k, a_ld, a_shift, bpw);
     else
-        hipLaunchKernelGGL(gemv_direct_kernel<false>, dim3(tiles), dim3(64 * waves), 0, s, a_i8, w_i8,
-                           a_scale, w_scale, out, m, n, k, bpw);
+        hipLaunchKernelGGL((gemv_direct_kernel<false, false>), grid, blk, 0, s, a_i8, w_i8, a_scale, w_scale,
+                           out, m, n, k, a_ld, a_shift, bpw);
     return hipGetLastError();
 }
 

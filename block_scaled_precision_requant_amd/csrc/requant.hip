@@ -36,15 +36,15 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
            ((uint32_t)d << 24);
 }
 
-// Quantize 8 values (BF16-representable) of a block whose 32 values sit on
-// the four lanes of a quad; returns the 8 codes packed and the block scale.
-__device__ __forceinline__ uint2 requant_a_vals(const float (&v)[8], float &s_out) {
+__device__ __forceinline__ float local_amax(const float (&v)[8]) {
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = quad_max(amax);
-    const float s = amax / 127.0f;
+    return amax;
+}
 
+// int8 codes of 8 values of a block with scale s = fl32(amax / 127).
+__device__ __forceinline__ uint2 int8_codes(const float (&v)[8], float s) {
     float t[8];
     if (s == 0.0f) {
 #pragma unroll
@@ -70,9 +70,44 @@ __device__ __forceinline__ uint2 requant_a_vals(const float (&v)[8], float &s_ou
                 if (near & (1u << i)) t[i] = rintf(v[i] / s);
         }
     }
-    s_out = s;
     return make_uint2(pack4_i8((int)t[0], (int)t[1], (int)t[2], (int)t[3]),
                       pack4_i8((int)t[4], (int)t[5], (int)t[6], (int)t[7]));
+}
+
+// Nearest OCP E4M3 code of x (ties to even, saturating at 448).  Normal
+// range: round the binary32 significand to 3 bits with an integer add (a
+// carry moves into the exponent); below 2^-6 the grid is m * 2^-9.
+__device__ __forceinline__ uint32_t e4m3_rne(float x) {
+    const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+    const float a = fminf(fabsf(x), 448.0f);
+    uint32_t code;
+    if (a < 0x1p-6f) {
+        code = (uint32_t)rintf(a * 512.0f);  // 8 is the smallest normal, code 0x08
+    } else {
+        const uint32_t b = __float_as_uint(a);
+        const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
+        code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
+    }
+    return sign | code;
+}
+
+// E4M3 codes of 8 values of a block with scale s = fl32(amax / 448).
+__device__ __forceinline__ uint2 e4m3_codes(const float (&v)[8], float s) {
+    if (s == 0.0f) return make_uint2(0u, 0u);
+    uint32_t c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = e4m3_rne(v[i] / s);  // IEEE divide, as the definition
+    return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                      c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+}
+
+// Quantize 8 values (BF16-representable) of a block whose 32 values sit on
+// the four lanes of a quad; returns the 8 codes packed and the block scale.
+__device__ __forceinline__ uint2 requant_a_vals(const float (&v)[8], float &s_out) {
+    const float amax = quad_max(local_amax(v));
+    const float s = amax / 127.0f;
+    s_out = s;
+    return int8_codes(v, s);
 }
 
 // One 16-byte chunk (8 BF16, element 2i in the low half of word i).
@@ -272,6 +307,87 @@ __global__ __launch_bounds__(kSiluThreads) void silu_requant_table_kernel(
     }
 }
 
+// ---- activation quantizers with other groups / E4M3 ----------------------
+// The W8A8 activation layouts of page "metrale_model_layers/layers/ops/
+// w8a8_decode/parts.rs" (scales per row or per (row, 128), E4M3 codes): the
+// per-32 rule with group size G and, for E4M3, 448 in place of 127 and the
+// nearest E4M3 code.
+
+// Max over the 16 lanes of a DPP row: quads, then rotations by 4 and 8.
+__device__ __forceinline__ float row16_max(float x) {
+    x = quad_max(x);
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, true)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true)));
+    return x;
+}
+
+__device__ __forceinline__ void bf16_chunk(uint4 raw, float (&v)[8]) {
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(wd[i] << 16);
+        v[2 * i + 1] = __uint_as_float(wd[i] & 0xFFFF0000u);
+    }
+}
+
+// Groups of LPG chunks (LPG = 4: 32 elements, 16: 128 elements) on LPG
+// consecutive lanes; U chunks per lane, kRqaThreads apart, loads first.
+template <bool E4M3, int LPG, int U>
+__global__ __launch_bounds__(kRqaThreads) void quant_group_kernel(const uint4 *__restrict__ a,
+                                                                  uint2 *__restrict__ q,
+                                                                  float *__restrict__ scale,
+                                                                  uint64_t nchunks) {
+    static_assert(LPG == 4 || LPG == 16, "group of 32 or 128 elements");
+    const uint64_t base = (uint64_t)blockIdx.x * kRqaThreads * U + threadIdx.x;
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) raw[u] = a[min(base + (uint64_t)u * kRqaThreads, nchunks - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        // nchunks is a multiple of LPG and so is every group's first chunk
+        const uint64_t c = base + (uint64_t)u * kRqaThreads;
+        float v[8];
+        bf16_chunk(raw[u], v);
+        const float amax = LPG == 4 ? quad_max(local_amax(v)) : row16_max(local_amax(v));
+        const float s = amax / (E4M3 ? 448.0f : 127.0f);
+        const uint2 codes = E4M3 ? e4m3_codes(v, s) : int8_codes(v, s);
+        if (c < nchunks) {
+            q[c] = codes;
+            if (c % LPG == 0) scale[c / LPG] = s;
+        }
+    }
+}
+
+// One scale per row: one workgroup per row, two passes over the row (the
+// second re-reads it from the caches).
+template <bool E4M3>
+__global__ __launch_bounds__(kRqaThreads) void quant_row_kernel(const uint4 *__restrict__ a,
+                                                                uint2 *__restrict__ q,
+                                                                float *__restrict__ scale, uint32_t kc) {
+    __shared__ float wmax[kRqaThreads / 64];
+    const uint64_t row0 = (uint64_t)blockIdx.x * kc;
+    float amax = 0.0f;
+    for (uint32_t c = threadIdx.x; c < kc; c += kRqaThreads) {
+        float v[8];
+        bf16_chunk(a[row0 + c], v);
+        amax = fmaxf(amax, local_amax(v));
+    }
+    amax = row16_max(amax);
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kRqaThreads / 64; ++w) amax = fmaxf(amax, wmax[w]);
+    const float s = amax / (E4M3 ? 448.0f : 127.0f);
+    for (uint32_t c = threadIdx.x; c < kc; c += kRqaThreads) {
+        float v[8];
+        bf16_chunk(a[row0 + c], v);
+        q[row0 + c] = E4M3 ? e4m3_codes(v, s) : int8_codes(v, s);
+    }
+    if (threadIdx.x == 0) scale[blockIdx.x] = s;
+}
+
 // OCP E4M3 code -> binary32.  Its exponent and mantissa bits shifted into a
 // binary32 give the value times 2^-120 (E4M3 subnormals land on binary32
 // subnormals), so one exact multiply restores it.
@@ -435,6 +551,27 @@ hipError_t launch_silu_requant(const uint16_t *gate, const uint16_t *up, uint32_
         const uint64_t grid = div_up(nchunks, (uint64_t)kRqaThreads * kRqaUnroll);
         hipLaunchKernelGGL(silu_requant_kernel<kRqaUnroll>, dim3((uint32_t)grid), dim3(kRqaThreads), 0, s,
                            gate, up, ld, reinterpret_cast<uint2 *>(a_i8), a_scale, nchunks, kc);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act(const uint16_t *a_bf16, uint8_t *q, float *scale, uint32_t m, uint32_t k,
+                            uint32_t group, bool e4m3, hipStream_t s) {
+    const uint32_t kc = k / 8;
+    const uint64_t nchunks = (uint64_t)m * kc;
+    const uint4 *a = reinterpret_cast<const uint4 *>(a_bf16);
+    uint2 *qq = reinterpret_cast<uint2 *>(q);
+    const dim3 blk(kRqaThreads);
+    const dim3 grid((uint32_t)div_up(nchunks, (uint64_t)kRqaThreads * kRqaUnroll));
+    if (group == 0) {
+        if (e4m3) hipLaunchKernelGGL(quant_row_kernel<true>, dim3(m), blk, 0, s, a, qq, scale, kc);
+        else hipLaunchKernelGGL(quant_row_kernel<false>, dim3(m), blk, 0, s, a, qq, scale, kc);
+    } else if (group == 32) {
+        if (e4m3) hipLaunchKernelGGL((quant_group_kernel<true, 4, kRqaUnroll>), grid, blk, 0, s, a, qq, scale, nchunks);
+        else hipLaunchKernelGGL((quant_group_kernel<false, 4, kRqaUnroll>), grid, blk, 0, s, a, qq, scale, nchunks);
+    } else {
+        if (e4m3) hipLaunchKernelGGL((quant_group_kernel<true, 16, kRqaUnroll>), grid, blk, 0, s, a, qq, scale, nchunks);
+        else hipLaunchKernelGGL((quant_group_kernel<false, 16, kRqaUnroll>), grid, blk, 0, s, a, qq, scale, nchunks);
     }
     return hipGetLastError();
 }

@@ -164,6 +164,49 @@ int silu_mul_requant_int8(const uint16_t *gate, const uint16_t *up, uint32_t ld,
 int w4a16_gemv(const uint16_t *x_bf16, const uint8_t *w_packed, const uint8_t *w_e4m3, float scale2,
                uint16_t *out, uint32_t m, uint32_t n, uint32_t k, void *stream);
 
+/* Activation code formats of quantize_act. */
+enum bsr_format {
+    BSR_FMT_INT8 = 0, /* int8 codes, scale = amax / 127                    */
+    BSR_FMT_E4M3 = 1  /* OCP E4M3 codes (bias 7, max 448), amax / 448      */
+};
+
+/*
+ * Activation quantizer with another scale layout: one F32 scale per group of
+ * `group` consecutive elements of a row (32 or 128) or per row (group = 0),
+ * int8 or E4M3 codes (the W8A8 activation layouts `W8a8Scale::PerRow` /
+ * `W8a8Scale::Block128` and the FP8 activation of page
+ * "metrale_model_layers/layers/ops/w8a8_decode/parts.rs"; the per-(row, 128)
+ * E4M3 quantizer of page ".../fp8_moe_grouped_tc_w8a8.rs").
+ *   a_bf16 [m, k]         BF16 as raw u16, 16-byte aligned, k % 32 == 0
+ *                         (k % 128 == 0 for group 128)
+ *   q      [m, k]         u8 codes (int8 two's complement or E4M3), 8-byte aligned
+ *   scale  [m, k / group] F32 ([m] for group 0), 4-byte aligned
+ * Per group: s = fl32(amax / F), F = 127 (int8) or 448 (E4M3); s == 0 gives
+ * scale +0 and codes 0; else q = clamp(rne(fl32(v / s)), -127, 127) for int8
+ * and the E4M3 code nearest fl32(v / s) (ties to the even code) for E4M3.
+ * group 32 with BSR_FMT_INT8 equals requant_a_int8.
+ * Errors: BSR_EINVAL (k, group, format), BSR_ENULL, BSR_EALIGN, BSR_EDEVICE,
+ * BSR_ELAUNCH.
+ */
+int quantize_act(const uint16_t *a_bf16, uint8_t *q, float *scale, uint32_t m, uint32_t k,
+                 uint32_t group, int format, void *stream);
+
+/*
+ * int8_gemm_blockscaled_ex with int8 activations whose scales come per group
+ * of a_group elements (32 or 128) or per row (a_group = 0), as quantize_act
+ * writes them: block b of row r is rescaled by fl32(a_scale[r, (32 b) /
+ * a_group] * w_scale[n, b]) (a_scale[r] for a_group 0), so the result equals
+ * int8_gemm_blockscaled with each activation scale repeated over its blocks.
+ *   a_scale [m, k / a_group] F32 ([m] for a_group 0), 4-byte aligned
+ * Other arguments, path and the output tolerance as int8_gemm_blockscaled_ex.
+ * Errors: BSR_EINVAL (a_group not 0/32/128, a_group 128 with k % 128 != 0,
+ * or as int8_gemm_blockscaled_ex), BSR_ENULL, BSR_EALIGN, BSR_EDEVICE,
+ * BSR_ELAUNCH.
+ */
+int int8_gemm_blockscaled_agroup(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
+                                 uint32_t a_group, const float *w_scale, uint16_t *out, uint32_t m,
+                                 uint32_t n, uint32_t k, void *stream, int path);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *bsr_status_string(int status);
 

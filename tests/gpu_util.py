@@ -74,3 +74,21 @@ def gpu_w4a16(x_bits, packed, e4m3, scale2):
     out = torch.empty((m, n), dtype=torch.int16, device=DEV)
     bsr.w4a16_gemv(x, wp, we, float(scale2), out)
     return out
+
+
+def gpu_quant_act(a_bits, group, fmt=bsr.FMT_INT8):
+    """group: 32, 128 or 0 (one scale per row)."""
+    a = to_dev(a_bits.view(np.int16))
+    m, k = a.shape
+    q = torch.empty((m, k), dtype=torch.uint8, device=DEV)
+    s = torch.empty((m, 1 if group == 0 else k // group), dtype=torch.float32, device=DEV)
+    bsr.quantize_act(a, q, s, group=group, fmt=fmt)
+    return q, s
+
+
+def gpu_gemm_agroup(a_i8, w_i8, a_s, group, w_s, path=bsr.PATH_AUTO):
+    m = a_i8.shape[0]
+    n = w_i8.shape[0]
+    out = torch.empty((m, n), dtype=torch.int16, device=DEV)
+    bsr.int8_gemm_blockscaled_agroup(a_i8, w_i8, a_s, group, w_s, out, path=path)
+    return out

@@ -114,3 +114,29 @@ def test_bad_scale2_and_path():
 def test_no_device_is_reported():
     L = bsr.lib()
     assert L.requant_a_int8(FAKE, FAKE, FAKE, 4, 64, None) == bsr.BSR_EDEVICE
+
+
+def test_quantize_act_validation():
+    L = bsr.lib()
+    null = None
+    assert L.quantize_act(FAKE, FAKE, FAKE, 4, 48, 32, 0, None) == bsr.BSR_EINVAL     # k
+    assert L.quantize_act(FAKE, FAKE, FAKE, 4, 96, 128, 0, None) == bsr.BSR_EINVAL    # k % 128
+    assert L.quantize_act(FAKE, FAKE, FAKE, 4, 128, 64, 0, None) == bsr.BSR_EINVAL    # group
+    assert L.quantize_act(FAKE, FAKE, FAKE, 4, 128, 32, 2, None) == bsr.BSR_EINVAL    # format
+    assert L.quantize_act(FAKE, FAKE, FAKE, 0, 128, 0, 1, None) == bsr.BSR_OK         # empty
+    assert L.quantize_act(null, FAKE, FAKE, 4, 128, 0, 1, None) == bsr.BSR_ENULL
+    assert L.quantize_act(FAKE, _fake(4), FAKE, 4, 128, 0, 1, None) == bsr.BSR_EALIGN
+    assert L.quantize_act(_fake(8), FAKE, FAKE, 4, 128, 32, 0, None) == bsr.BSR_EALIGN
+
+
+def test_gemm_agroup_validation():
+    L = bsr.lib()
+    args = (FAKE, FAKE, FAKE)
+    assert L.int8_gemm_blockscaled_agroup(*args, 64, FAKE, FAKE, 4, 4, 128, None, 0) == bsr.BSR_EINVAL
+    assert L.int8_gemm_blockscaled_agroup(*args, 128, FAKE, FAKE, 4, 4, 96, None, 0) == bsr.BSR_EINVAL
+    assert L.int8_gemm_blockscaled_agroup(*args, 0, FAKE, FAKE, 4, 4, 48, None, 0) == bsr.BSR_EINVAL
+    assert L.int8_gemm_blockscaled_agroup(*args, 0, FAKE, FAKE, 9, 4, 96, None, 2) == bsr.BSR_EINVAL  # gemv m>8
+    assert L.int8_gemm_blockscaled_agroup(*args, 0, FAKE, FAKE, 4, 4, 96, None, 7) == bsr.BSR_EINVAL  # path
+    assert L.int8_gemm_blockscaled_agroup(*args, 128, FAKE, FAKE, 0, 4, 256, None, 0) == bsr.BSR_OK
+    assert L.int8_gemm_blockscaled_agroup(FAKE, FAKE, None, 128, FAKE, FAKE, 4, 4, 256, None, 0) == bsr.BSR_ENULL
+    assert L.int8_gemm_blockscaled_agroup(FAKE, FAKE, _fake(2), 0, FAKE, FAKE, 4, 4, 256, None, 0) == bsr.BSR_EALIGN
