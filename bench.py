@@ -46,7 +46,7 @@ def _args():
     p.add_argument("--decode-iters", type=int, default=100)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
-    p.add_argument("--only", choices=["all", "prefill", "decode", "silu", "copy"], default="all",
+    p.add_argument("--only", choices=["all", "prefill", "decode", "silu", "layouts", "copy"], default="all",
                    help="copy: a plain 256 MiB device copy, the known-size reference for HBM byte counters")
     return p.parse_args()
 
@@ -273,6 +273,60 @@ def main():
         del ssets
         torch.cuda.empty_cache()
 
+    # ------------------------------------------------------------ other activation layouts
+    if args.only in ("all", "layouts"):
+        lay = {}
+        qbytes = {32: M * K * (2 + 1 + 4 / 32), 128: M * K * (2 + 1 + 4 / 128), 0: M * K * 3 + 4 * M}
+        nq = max(2, int(np.ceil(2 ** 30 / (M * K * 3))))
+        a_copies = [dev_t(a_bits.view(np.int16)) for _ in range(nq)]
+        q_buf = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        for fmt, fname in ((bsr.FMT_INT8, "int8"), (bsr.FMT_E4M3, "e4m3")):
+            for g in (32, 128, 0):
+                s_buf = torch.empty((M, 1 if g == 0 else K // g), dtype=torch.float32, device=dev)
+                t_q = burst(lambda i: bsr.quantize_act(a_copies[i % nq], q_buf, s_buf, group=g, fmt=fmt,
+                                                       stream=stream), max(20, 2 * nq))
+                gname = "row" if g == 0 else str(g)
+                lay[f"quantize_act_{fname}_g{gname}"] = dict(us_burst=t_q * 1e6, gbs=qbytes[g] / t_q / 1e9,
+                                                              frac_hbm=qbytes[g] / t_q / 1e9 / PEAK_HBM_GBS)
+        del a_copies
+        w_i8 = torch.empty((N, K), dtype=torch.int8, device=dev)
+        w_s = torch.empty((N, K // 32), dtype=torch.float32, device=dev)
+        bsr.requant_w_nvfp4_int8(dev_t(packed), dev_t(e4m3), scale2, w_i8, w_s)
+        a_dev = dev_t(a_bits.view(np.int16))
+        out = torch.empty((M, N), dtype=torch.int16, device=dev)
+        for g in (32, 128, 0):
+            s_buf = torch.empty((M, 1 if g == 0 else K // g), dtype=torch.float32, device=dev)
+            bsr.quantize_act(a_dev, q_buf, s_buf, group=g, stream=stream)
+            t_g = burst(lambda i: bsr.int8_gemm_blockscaled_agroup(q_buf.view(torch.int8), w_i8, s_buf, g, w_s, out,
+                                                                   stream=stream), 20)
+            gname = "row" if g == 0 else str(g)
+            lay[f"gemm_agroup_g{gname}"] = dict(us_burst=t_g * 1e6, tops=2.0 * M * N * K / t_g / 1e12)
+        del w_i8, w_s
+        # decode GEMV with grouped activation scales (M=8, N=4096, K=14336)
+        p = [q for q in inputs.workload("decode").projections if q.name == "decode_m8_n4096_k14336"][0]
+        wp, we = p.weight()
+        w_i8 = torch.empty((p.n, p.k), dtype=torch.int8, device=dev)
+        w_s = torch.empty((p.n, p.k // 32), dtype=torch.float32, device=dev)
+        bsr.requant_w_nvfp4_int8(dev_t(wp), dev_t(we), float(p.scale2), w_i8, w_s)
+        ncopy = max(2, int(np.ceil(2 ** 30 / (p.n * p.k * 1.125))))
+        copies = [(w_i8.clone(), w_s.clone()) for _ in range(ncopy)]
+        xa = dev_t(p.activations().view(np.int16))
+        xq = torch.empty((p.m, p.k), dtype=torch.uint8, device=dev)
+        xo = torch.empty((p.m, p.n), dtype=torch.int16, device=dev)
+        for g in (32, 128, 0):
+            xs = torch.empty((p.m, 1 if g == 0 else p.k // g), dtype=torch.float32, device=dev)
+            bsr.quantize_act(xa, xq, xs, group=g, stream=stream)
+            t_v = burst(lambda i: bsr.int8_gemm_blockscaled_agroup(xq.view(torch.int8), copies[i % ncopy][0], xs, g,
+                                                                   copies[i % ncopy][1], xo, stream=stream),
+                        args.decode_iters)
+            alg = p.n * p.k * 1.125 + p.m * p.k + xs.numel() * 4 + 2 * p.m * p.n
+            gname = "row" if g == 0 else str(g)
+            lay[f"gemv_agroup_g{gname}_{p.name}"] = dict(us_burst=t_v * 1e6, gbs=alg / t_v / 1e9,
+                                                        frac_hbm=alg / t_v / 1e9 / PEAK_HBM_GBS)
+        del copies
+        torch.cuda.empty_cache()
+        rec["layouts"] = lay
+
     # ------------------------------------------------------------ CPU oracle
     cpu = None
     if not args.no_cpu_baseline and args.only in ("all", "prefill"):
@@ -332,6 +386,8 @@ def main():
         line["decode"] = rec["decode"]
     if "silu" in rec:
         line["silu_mul_requant"] = rec["silu"]
+    if "layouts" in rec:
+        line["activation_layouts"] = rec["layouts"]
     print(json.dumps(line), flush=True)
 
 
