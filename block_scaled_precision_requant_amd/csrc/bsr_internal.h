@@ -26,11 +26,9 @@ constexpr int kSiluThreads = 512;    // lanes per workgroup of the SiLU table ke
 // made of 32 x 32 MFMA tiles.  The K loop stages kGemmStageBlocks 32-wide
 // blocks of A, W and their scales per LDS buffer, in a ring of kGemmRing
 // buffers.  Workgroups are ordered so that each XCD runs a compact
-// kGemmGroupM-tall group of output tiles.  Three shapes are built: 128 x 128
-// with sixteen 32 x 32 waves (m <= 128), 256 x 128 with eight 64 x 64 waves
-// (grids of up to two rounds over the CUs), and 128 x 128 with four 64 x 64
-// waves and two workgroups per CU (larger grids).
-constexpr int kGemmBMLarge = 256;
+// kGemmGroupM-tall group of output tiles.  Two shapes are built, both 128 x
+// 128: sixteen 32 x 32 waves (m <= 128), and four 64 x 64 waves with two
+// workgroups per CU (m > 128).
 constexpr int kGemmBMSmall = 128;
 constexpr int kGemmBN = 128;
 constexpr int kGemmStageBlocks = 4;

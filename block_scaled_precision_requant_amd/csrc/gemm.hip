@@ -328,13 +328,10 @@ hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_sc
     if (m <= (uint32_t)kGemmBMSmall)
         return launch_tiles<kGemmBMSmall, kGemmBN, 32, 32, 1>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, a_ld,
                                                               a_shift, s);
-    // Up to two rounds of 256x128 tiles over the CUs: one 8-wave workgroup per
-    // CU.  Larger grids: two 4-wave 128x128 workgroups per CU, whose barriers
-    // fall at different times, so one computes while the other waits.
-    const uint64_t big_tiles = div_up(m, kGemmBMLarge) * div_up(n, kGemmBN);
-    if (big_tiles <= 2 * (uint64_t)kGemmCus)
-        return launch_tiles<kGemmBMLarge, kGemmBN, 64, 64, 1>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, a_ld,
-                                                              a_shift, s);
+    // Larger m: two 4-wave 128x128 workgroups per CU (LDS 2 x 72 KB, 2 x 4
+    // waves of about 230 VGPRs).  Their barriers fall at different times, so
+    // one computes while the other waits; measured faster than one 8-wave
+    // 256x128 workgroup per CU at 2048x4096x4096 as well as at 4096x28672x4096.
     return launch_tiles<kGemmBMSmall, kGemmBN, 64, 64, 2>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, a_ld,
                                                           a_shift, s);
 }
