@@ -14,7 +14,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsr.so")
 
 BSR_OK, BSR_EINVAL, BSR_ENULL, BSR_EALIGN, BSR_EDEVICE, BSR_ELAUNCH = range(6)
-PATH_AUTO, PATH_GEMM, PATH_GEMV = 0, 1, 2
+PATH_AUTO, PATH_GEMM, PATH_GEMV, PATH_INVARIANT = 0, 1, 2, 3
 GEMV_MAX_ROWS = 8
 
 # Exported symbols and their C signatures (kept in step with include/bsr.h).

@@ -40,7 +40,8 @@ int gemm_args_check(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale
                     const float *w_scale, const uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                     int path) {
     if (!k_ok(k)) return BSR_EINVAL;
-    if (path != BSR_PATH_AUTO && path != BSR_PATH_GEMM && path != BSR_PATH_GEMV) return BSR_EINVAL;
+    if (path != BSR_PATH_AUTO && path != BSR_PATH_GEMM && path != BSR_PATH_GEMV && path != BSR_PATH_INVARIANT)
+        return BSR_EINVAL;
     if (m == 0 || n == 0) return BSR_OK;
     if (path == BSR_PATH_GEMV && m > (uint32_t)bsr::kGemvMaxRows) return BSR_EINVAL;
     if (!a_i8 || !w_i8 || !a_scale || !w_scale || !out) return BSR_ENULL;
@@ -113,8 +114,11 @@ int gemm_launch(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, ui
                 uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                 void *stream, int path) {
     if (int st = check_device()) return st;
-    const bool gemv = path == BSR_PATH_GEMV || (path == BSR_PATH_AUTO && m <= (uint32_t)bsr::kGemvMaxRows);
+    const bool small = m <= (uint32_t)bsr::kGemvMaxRows;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (path == BSR_PATH_INVARIANT && small)
+        return launched(bsr::launch_gemv_chain(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s));
+    const bool gemv = path == BSR_PATH_GEMV || (path == BSR_PATH_AUTO && small);
     if (gemv) return launched(bsr::launch_gemv(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s));
     return launched(bsr::launch_gemm(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s));
 }

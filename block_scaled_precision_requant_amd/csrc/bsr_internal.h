@@ -72,6 +72,10 @@ hipError_t launch_quant_act(const uint16_t *a_bf16, uint8_t *q, float *scale, ui
 hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
                        uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
                        uint32_t k, hipStream_t s);
+// GEMV whose per-output accumulation follows the GEMM's block order.
+hipError_t launch_gemv_chain(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
+                             uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
+                             uint32_t k, hipStream_t s);
 hipError_t launch_gemv(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
                        uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
                        uint32_t k, hipStream_t s);

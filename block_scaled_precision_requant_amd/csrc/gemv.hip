@@ -24,7 +24,10 @@
 //    only global loads of the K loop are weight bytes -- one 1 KB instruction
 //    per wave step;
 //  * direct: every operand comes from global memory.  Used when the staged
-//    copies do not fit in LDS or K is not a multiple of 128.
+//    copies do not fit in LDS or K is not a multiple of 128;
+//  * chain: one wave per workgroup runs all of K in block order, so each
+//    output is the same FP32 chain acc = fma(P_b, fl32(a_s * w_s), acc),
+//    b = 0, 1, ..., that the GEMM evaluates -- its BF16 bits equal the GEMM's.
 #include "bsr_internal.h"
 
 namespace bsr {
@@ -168,6 +171,77 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void gemv_direct_kernel(
     gemv_reduce_store(red, acc, wave, nwaves, lane, n0, m, n, out);
 }
 
+// ---------------------------------------------------------------- chain
+
+constexpr int kChainDepth = 4;  // iterations whose loads are in flight ahead of the compute
+
+// One wave, 16 columns, all of K in increasing block order: per output, the
+// blocks' rescaled products enter a single FP32 accumulator in the GEMM's
+// order, which makes the result independent of the path and of m.  Loads run
+// kChainDepth iterations ahead in a register ring (the ring index is static
+// in the unrolled body); past the last iteration they re-read it.
+template <bool VEC, bool AGROUP>
+__global__ __launch_bounds__(64) void gemv_chain_kernel(
+    const int8_t *__restrict__ a, const int8_t *w, const float *__restrict__ a_s,
+    const float *__restrict__ w_s, uint16_t *__restrict__ out, uint32_t m, uint32_t n, uint32_t k,
+    uint32_t a_ld, uint32_t a_shift) {
+    const int lane = threadIdx.x & 63;
+    const int q = lane >> 4;
+    const uint32_t n0 = blockIdx.x * kGemvCols;
+    const uint32_t col = min(n0 + (lane & 15), n - 1);
+    const uint32_t arow = lane & 15;
+    const bool a_live = arow < m;
+    const uint32_t nb = k / 32;
+    const uint32_t niter = (nb + kGemvBlocksPerIter - 1) / kGemvBlocksPerIter;
+    const uint32_t srow0 = min(4u * (uint32_t)q, m - 1);
+
+    const int8_t *wrow = w + (uint64_t)col * k;
+    const int8_t *arowp = a + (uint64_t)min(arow, m - 1) * k;
+    const float *wsrow = w_s + (uint64_t)col * nb;
+    auto load = [&](IterOps &x, uint32_t it) {
+        const uint32_t b0 = it * kGemvBlocksPerIter;
+#pragma unroll
+        for (int t = 0; t < kSteps; ++t) {
+            const uint64_t off = min((uint64_t)b0 * 32 + 64 * t + 16 * q, (uint64_t)k - 16);
+            x.wv[t] = *reinterpret_cast<const v4i *>(wrow + off);
+            x.av[t] = *reinterpret_cast<const v4i *>(arowp + off);
+        }
+#pragma unroll
+        for (int h = 0; h < kQuads; ++h) {
+            x.wsv[h] = load_f4<VEC>(wsrow, b0 + 4 * h, nb);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float *ar = a_s + (uint64_t)min(srow0 + r, m - 1) * a_ld;
+                x.asv[h][r] = AGROUP ? load_group_f4(ar, b0 + 4 * h, nb, a_shift) : load_f4<VEC>(ar, b0 + 4 * h, nb);
+            }
+        }
+    };
+
+    IterOps ring[kChainDepth];
+#pragma unroll
+    for (int u = 0; u < kChainDepth; ++u) load(ring[u], min((uint32_t)u, niter - 1));
+    asm volatile("" ::: "memory");
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (uint32_t it0 = 0; it0 < niter; it0 += kChainDepth) {
+#pragma unroll
+        for (int u = 0; u < kChainDepth; ++u) {
+            // past the last iteration every block is >= nb: zero activations, P = 0,
+            // and acc + 0 * s leaves acc unchanged (acc is never -0)
+            gemv_iter(acc, ring[u], (it0 + u) * kGemvBlocksPerIter, nb, a_live, q);
+            load(ring[u], min(it0 + u + kChainDepth, niter - 1));
+            // keep the refill here: the compiler would otherwise sink it to its
+            // use kChainDepth iterations later and the loads would not overlap
+            asm volatile("" ::: "memory");
+        }
+    }
+    const uint32_t c = n0 + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t row = 4 * q + r;
+        if (row < m && c < n) out[(uint64_t)row * n + c] = f32_to_bf16_rne(acc[r]);
+    }
+}
+
 // ---------------------------------------------------------------- staged
 
 // Each wave stages the slices of A, a_s and w_s that its own K range needs
@@ -308,6 +382,23 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void gemv_staged_kernel(
 }
 
 }  // namespace
+
+hipError_t launch_gemv_chain(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
+                             uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
+                             uint32_t k, hipStream_t s) {
+    const dim3 grid((uint32_t)div_up(n, kGemvCols)), blk(64);
+    const uint32_t nb = k / 32;
+    if (a_shift)
+        hipLaunchKernelGGL((gemv_chain_kernel<false, true>), grid, blk, 0, s, a_i8, w_i8, a_scale, w_scale, out,
+                           m, n, k, a_ld, a_shift);
+    else if (nb % 4 == 0)
+        hipLaunchKernelGGL((gemv_chain_kernel<true, false>), grid, blk, 0, s, a_i8, w_i8, a_scale, w_scale, out,
+                           m, n, k, a_ld, a_shift);
+    else
+        hipLaunchKernelGGL((gemv_chain_kernel<false, false>), grid, blk, 0, s, a_i8, w_i8, a_scale, w_scale, out,
+                           m, n, k, a_ld, a_shift);
+    return hipGetLastError();
+}
 
 hipError_t launch_gemv(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
                        uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,

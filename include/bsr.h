@@ -113,7 +113,16 @@ int int8_gemm_blockscaled(const int8_t *a_i8, const int8_t *w_i8, const float *a
 enum bsr_path {
     BSR_PATH_AUTO = 0, /* GEMV iff m <= 8, as int8_gemm_blockscaled     */
     BSR_PATH_GEMM = 1, /* the MFMA GEMM at any m                         */
-    BSR_PATH_GEMV = 2  /* the GEMV; requires m <= 8, else BSR_EINVAL     */
+    BSR_PATH_GEMV = 2, /* the GEMV; requires m <= 8, else BSR_EINVAL     */
+    BSR_PATH_INVARIANT = 3 /* m <= 8: a GEMV that accumulates every output
+                            * over the K blocks in increasing order, as the
+                            * GEMM does; m > 8: the GEMM.  A row's output
+                            * bits then depend on neither m nor the path
+                            * (the invariants stated for `W8a8Weight::segment`
+                            * on page "metrale_model_layers/layers/ops/
+                            * w8a8_decode/parts.rs" and for `nvfp4_proj_mx`
+                            * on page ".../w4a4_proj/fixed.rs"); slower
+                            * decode than BSR_PATH_GEMV, whose waves split K */
 };
 
 /*

@@ -105,7 +105,8 @@ def test_bad_scale2_and_path():
     L = bsr.lib()
     for s2 in (float("nan"), float("inf"), -float("inf")):
         assert L.requant_w_nvfp4_int8(FAKE, FAKE, s2, FAKE, FAKE, 4, 64, None) == bsr.BSR_EINVAL
-    assert L.int8_gemm_blockscaled_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 64, None, 3) == bsr.BSR_EINVAL
+    assert L.int8_gemm_blockscaled_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 64, None, 4) == bsr.BSR_EINVAL
+    assert L.int8_gemm_blockscaled_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 64, None, -1) == bsr.BSR_EINVAL
     assert L.int8_gemm_blockscaled_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 9, 4, 64, None,
                                       bsr.PATH_GEMV) == bsr.BSR_EINVAL
 
