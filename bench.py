@@ -232,6 +232,9 @@ def main():
             e1.record(stream)
             torch.cuda.synchronize()
             t_qv = e0.elapsed_time(e1) * 1e-3 / it
+            # the path-invariant GEMV (one FP32 chain per output, in the GEMM's order)
+            t_inv = burst(lambda i: bsr.int8_gemm_blockscaled_ex(a_i8, copies[i % ncopy][0], a_s, copies[i % ncopy][1],
+                                                                 out, path=bsr.PATH_INVARIANT, stream=stream), it)
             alg = p.n * p.k * 1.125 + p.m * p.k * 1.125 + 2 * p.m * p.n
             del copies
             # W4A16: the same product straight from the NVFP4 weight (0.5625 B per weight)
@@ -246,6 +249,8 @@ def main():
             dec[p.name] = dict(m=p.m, n=p.n, k=p.k, gemv_us_burst=t_v * 1e6,
                                gemv_gbs=alg / t_v / 1e9, gemv_frac_hbm=alg / t_v / 1e9 / PEAK_HBM_GBS,
                                requant_a_plus_gemv_us_burst=t_qv * 1e6,
+                               invariant_gemv_us_burst=t_inv * 1e6,
+                               invariant_gemv_frac_hbm=alg / t_inv / 1e9 / PEAK_HBM_GBS,
                                w4a16_us_burst=t_4 * 1e6, w4a16_gbs=alg4 / t_4 / 1e9,
                                w4a16_frac_hbm=alg4 / t_4 / 1e9 / PEAK_HBM_GBS)
             del copies4
