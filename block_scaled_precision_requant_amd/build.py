@@ -28,9 +28,15 @@ FLAGS = [
 ]
 
 
+# Per-source additions: the GEMV kernels' matrix-core results are consumed by
+# vector FP32 code, so they must land in ordinary VGPRs (the default heuristic
+# puts them in AGPRs for one-wave workgroups, costing a copy per value).
+EXTRA_FLAGS = {"gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src, save_temps):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if save_temps:
         cmd.insert(1, f"-save-temps={'obj'}")
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -28,6 +28,8 @@
 //  * chain: one wave per workgroup runs all of K in block order, so each
 //    output is the same FP32 chain acc = fma(P_b, fl32(a_s * w_s), acc),
 //    b = 0, 1, ..., that the GEMM evaluates -- its BF16 bits equal the GEMM's.
+#include <type_traits>
+
 #include "bsr_internal.h"
 
 namespace bsr {
@@ -242,6 +244,188 @@ __global__ __launch_bounds__(64) void gemv_chain_kernel(
     }
 }
 
+// Streamed chain kernel (K a multiple of 128): the same FP32 chain, with W, A
+// and both scales brought into an LDS ring by global_load_lds in chunks of
+// kChainChunkBlocks blocks, so the wave's only waits are for a whole chunk
+// that was requested one chunk earlier.  The block products come from
+// v_mfma_i32_16x16x32_i8 (K = 32: one block, no zeroed operand quarters):
+// lane (c = l % 16, q = l / 16) gives bytes 8q..8q+7 of a block of
+// activation row c and of weight row n0 + c; A and B pair by (quarter, byte),
+// so the sum over lanes is the block's exact dot product.
+constexpr int kChainChunkBlocks = 32;
+constexpr int kChainRowPitch = kChainChunkBlocks * 32 + 16;  // bytes; +16 spreads 16 rows over the banks
+constexpr int kChainSPitch = kChainChunkBlocks + 4;          // floats per scale row
+constexpr int kChainARows = kGemvMaxRows;
+constexpr int kChainSRows = kGemvCols + kChainARows;         // w_s rows, then a_s rows
+
+struct ChainBuf {
+    int8_t w[kGemvCols * kChainRowPitch];
+    int8_t a[kChainARows * kChainRowPitch];
+    float s[kChainSRows * kChainSPitch];
+};
+
+// Copies of one chunk issued by the wave: one 1 KB copy per weight and
+// activation row, the scale rows flattened into 16-byte copies (4-byte copies
+// for grouped activation scales, expanded to one per block).  Every copy
+// instruction has live lanes, so each one counts once in vmcnt.
+template <bool AGROUP>
+struct ChainCopies {
+    static constexpr int kScale16 = AGROUP ? (kGemvCols * kChainSPitch + 255) / 256
+                                           : (kChainSRows * kChainSPitch + 255) / 256;
+    static constexpr int kScale4 = AGROUP ? (kChainARows * kChainSPitch + 63) / 64 : 0;
+    static constexpr int kTotal = kGemvCols + kChainARows + kScale16 + kScale4;
+};
+
+// Operands of one iteration (4 blocks) of the streamed chain kernel: per
+// block 8 activation and 8 weight bytes, and the scale pair this lane feeds
+// into the scale-product MFMA (activation row l % 16, weight column l % 16,
+// block l / 16 of the iteration).
+struct ChainOps {
+    long av[4], wv[4];
+    float as, ws;
+};
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+template <bool AGROUP, int RING>
+__global__ __launch_bounds__(64) void gemv_chain_lds_kernel(
+    const int8_t *__restrict__ a, const int8_t *w, const float *__restrict__ a_s,
+    const float *__restrict__ w_s, uint16_t *__restrict__ out, uint32_t m, uint32_t n, uint32_t k,
+    uint32_t a_ld, uint32_t a_shift) {
+    __shared__ __attribute__((aligned(16))) ChainBuf ring[RING];
+    constexpr int NC = ChainCopies<AGROUP>::kTotal;
+    static_assert(NC * (RING - 1) < 64, "the copies in flight fit the vmcnt range");
+
+    const int lane = threadIdx.x & 63;
+    const int q = lane >> 4;
+    const uint32_t c16 = lane & 15;
+    const uint32_t n0 = blockIdx.x * kGemvCols;
+    const uint32_t nb = k / 32;  // a multiple of 4
+    const uint32_t nchunks = (nb + kChainChunkBlocks - 1) / kChainChunkBlocks;
+
+    auto issue = [&](int bi, uint32_t chunk) {
+        ChainBuf &b = ring[bi];
+        // row bases are wave-uniform (scalar registers); lanes add a 32-bit offset
+        const uint32_t off = min(chunk * (uint32_t)kChainChunkBlocks * 32 + 16 * lane, k - 16);
+#pragma unroll
+        for (int r = 0; r < kGemvCols; ++r) {
+            const int8_t *row = w + (uint64_t)min(n0 + r, n - 1) * k;
+            __builtin_amdgcn_global_load_lds(row + off, (lds_void *)(b.w + r * kChainRowPitch), 16, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < kChainARows; ++r) {
+            const int8_t *row = a + (uint64_t)min((uint32_t)r, m - 1) * k;
+            __builtin_amdgcn_global_load_lds(row + off, (lds_void *)(b.a + r * kChainRowPitch), 16, 0, 0);
+        }
+        const uint32_t bb0 = chunk * kChainChunkBlocks;
+        constexpr uint32_t s_rows16 = AGROUP ? kGemvCols : kChainSRows;
+#pragma unroll
+        for (int i = 0; i < ChainCopies<AGROUP>::kScale16; ++i) {
+            const uint32_t p = i * 256 + 4 * lane;  // float index in the region
+            const uint32_t r = min(p / kChainSPitch, s_rows16 - 1);
+            const uint32_t cb = min(bb0 + min(p % kChainSPitch, (uint32_t)kChainChunkBlocks - 4), nb - 4);
+            const float *src = r < kGemvCols ? w_s + (uint64_t)min(n0 + r, n - 1) * nb + cb
+                                             : a_s + (uint64_t)min(r - kGemvCols, m - 1) * a_ld + cb;
+            if (p < s_rows16 * kChainSPitch)  // lanes past the region stay idle
+                __builtin_amdgcn_global_load_lds(src, (lds_void *)(b.s + i * 256), 16, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < ChainCopies<AGROUP>::kScale4; ++i) {
+            const uint32_t p = i * 64 + lane;
+            const uint32_t r = min(p / kChainSPitch, (uint32_t)kChainARows - 1);
+            const uint32_t cb = min(bb0 + min(p % kChainSPitch, (uint32_t)kChainChunkBlocks - 1), nb - 1);
+            if (p < kChainARows * kChainSPitch)
+                __builtin_amdgcn_global_load_lds(a_s + (uint64_t)min(r, m - 1) * a_ld + (cb >> a_shift),
+                                                 (lds_void *)(b.s + kGemvCols * kChainSPitch + i * 64), 4, 0, 0);
+        }
+    };
+
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    // One chunk from LDS: blocks in increasing order, one FP32 chain per
+    // output; each iteration's LDS reads are issued before the previous
+    // iteration's arithmetic, which hides their latency.
+    auto compute = [&](int bi, uint32_t chunk, auto full_chunk) {
+        constexpr bool full = decltype(full_chunk)::value;
+        const ChainBuf &b = ring[bi];
+        const int8_t *wr = b.w + c16 * kChainRowPitch + 8 * q;
+        const int8_t *ar = b.a + min(c16, (uint32_t)kChainARows - 1) * kChainRowPitch + 8 * q;
+        const float *wsr = b.s + c16 * kChainSPitch + q;
+        const float *asr = b.s + (kGemvCols + min(c16, m - 1)) * kChainSPitch + q;
+        auto read = [&](ChainOps &x, int i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x.av[j] = *reinterpret_cast<const long *>(ar + (4 * i + j) * 32);
+                x.wv[j] = *reinterpret_cast<const long *>(wr + (4 * i + j) * 32);
+            }
+            x.as = asr[4 * i];
+            x.ws = wsr[4 * i];
+        };
+        const uint32_t bb0 = chunk * kChainChunkBlocks;
+        const v4i zero4 = {0, 0, 0, 0};
+        const v16f zero16 = {};
+        ChainOps x[2];
+        read(x[0], 0);
+#pragma unroll
+        for (int i = 0; i < kChainChunkBlocks / 4; ++i) {
+            if (i + 1 < kChainChunkBlocks / 4) read(x[(i + 1) & 1], i + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const ChainOps &cur = x[i & 1];
+            v4i p[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // only the last chunk can hold blocks past K: zero activations
+                // there, so P = 0 and acc + 0 * s = acc
+                const long avl = (full || bb0 + 4 * i + j < nb) ? cur.av[j] : 0;
+                p[j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(avl, cur.wv[j], zero4, 0, 0, 0);
+            }
+            // the 4 blocks' scale outer products a_s x w_s, one rounded product
+            // per output: block j in registers 4j..4j+3, laid out like P
+            const v16f sc = __builtin_amdgcn_mfma_f32_16x16x1f32(cur.as, cur.ws, zero16, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = fmaf((float)p[j][r], sc[4 * j + r], acc[r]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // Reads of a buffer are complete before copies into it are issued.
+    auto reads_done = [&]() {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt at their maxima
+        asm volatile("" ::: "memory");
+    };
+    // Before computing chunk c: wait for its copies; the copies of the chunks
+    // after it that were issued (at most RING - 1) may stay in flight.
+    auto wait_chunk = [&](uint32_t c) {
+        const uint32_t ahead = min(nchunks - 1 - c, (uint32_t)RING - 1);
+        if (RING > 2 && ahead >= 2) wait_vm_le<NC * (RING - 1 > 1 ? 2 : 1)>();
+        else if (ahead >= 1) wait_vm_le<NC>();
+        else wait_vm_le<0>();
+        asm volatile("" ::: "memory");
+    };
+
+#pragma unroll
+    for (int r = 0; r < RING - 1; ++r)
+        if ((uint32_t)r < nchunks) issue(r, r);
+    for (uint32_t c0 = 0; c0 < nchunks; c0 += RING) {
+#pragma unroll
+        for (int u = 0; u < RING; ++u) {
+            const uint32_t c = c0 + u;
+            if (c >= nchunks) break;
+            // buffer (u + RING - 1) % RING held chunk c - 1, whose reads are done
+            if (c + RING - 1 < nchunks) issue((u + RING - 1) % RING, c + RING - 1);
+            wait_chunk(c);
+            if ((c + 1) * kChainChunkBlocks <= nb) compute(u, c, std::true_type());
+            else compute(u, c, std::false_type());
+            reads_done();
+        }
+    }
+    const uint32_t col = n0 + c16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t row = 4 * q + r;
+        if (row < m && col < n) out[(uint64_t)row * n + col] = f32_to_bf16_rne(acc[r]);
+    }
+}
+
 // ---------------------------------------------------------------- staged
 
 // Each wave stages the slices of A, a_s and w_s that its own K range needs
@@ -388,6 +572,20 @@ hipError_t launch_gemv_chain(const int8_t *a_i8, const int8_t *w_i8, const float
                              uint32_t k, hipStream_t s) {
     const dim3 grid((uint32_t)div_up(n, kGemvCols)), blk(64);
     const uint32_t nb = k / 32;
+    if (nb % 4 == 0) {
+        // few column tiles: one workgroup per CU, so a deeper ring costs nothing
+        const bool deep = grid.x <= (uint32_t)kGemmCus;
+        if (a_shift)  // (its 32 copies per chunk allow one chunk in flight)
+            hipLaunchKernelGGL((gemv_chain_lds_kernel<true, 2>), grid, blk, 0, s, a_i8, w_i8, a_scale, w_scale,
+                               out, m, n, k, a_ld, a_shift);
+        else if (deep)
+            hipLaunchKernelGGL((gemv_chain_lds_kernel<false, 3>), grid, blk, 0, s, a_i8, w_i8, a_scale, w_scale,
+                               out, m, n, k, a_ld, a_shift);
+        else
+            hipLaunchKernelGGL((gemv_chain_lds_kernel<false, 2>), grid, blk, 0, s, a_i8, w_i8, a_scale, w_scale,
+                               out, m, n, k, a_ld, a_shift);
+        return hipGetLastError();
+    }
     if (a_shift)
         hipLaunchKernelGGL((gemv_chain_kernel<false, true>), grid, blk, 0, s, a_i8, w_i8, a_scale, w_scale, out,
                            m, n, k, a_ld, a_shift);
