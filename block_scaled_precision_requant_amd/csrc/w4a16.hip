@@ -103,10 +103,13 @@ __host__ __device__ inline uint32_t w4_pitch(uint32_t pass_steps) { return pass_
 // bytes for a pass with 16-byte loads (8 bytes per super-step); otherwise it
 // reads its own two codes per super-step with 2-byte loads.
 // PS: super-steps per staging pass (at most kW4PassSteps; even when VS).
+// CT: 16-column tiles per workgroup; each wave runs all CT tiles over its K
+// range with one staged copy of the activations, so larger m (whose
+// activation bytes rival the weight bytes) copies them fewer times.
 // (wp and we are not __restrict__: a restrict-qualified read-only load may be
 // moved past the empty asm statements that keep a pass's loads ahead of its
 // compute.)
-template <bool VS, int PS>
+template <bool VS, int PS, int CT>
 __global__ __launch_bounds__(kGemvMaxWaves * 64) void w4a16_kernel(
     const uint16_t *__restrict__ x, const uint8_t *wp, const uint8_t *we,
     float scale2, uint16_t *__restrict__ out, uint32_t m, uint32_t n, uint32_t k, uint32_t steps_per_wave) {
@@ -119,18 +122,25 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void w4a16_kernel(
     const int nwaves = blockDim.x >> 6;
     const int q = lane >> 4;
     const uint32_t c = lane & 15;
-    const uint32_t n0 = blockIdx.x * kGemvCols;
-    const uint32_t col = min(n0 + c, n - 1);
+    const uint32_t n0 = blockIdx.x * kGemvCols * CT;
     const uint32_t nsteps = (k + kStepK - 1) / kStepK;
     const uint32_t s_begin = wave * steps_per_wave;
     const uint32_t s_end = min(nsteps, s_begin + steps_per_wave);
     const uint32_t pitch = w4_pitch(pass_steps);
     int8_t *la = smem + (uint64_t)wave * (m * pitch);
     const uint32_t arow = min(c, m - 1);  // activation row this lane feeds
-    const uint8_t *wrow = wp + (uint64_t)col * (k / 2);
-    const uint8_t *srow = we + (uint64_t)col * (k / 16);
+    const uint8_t *wrow[CT];
+    const uint8_t *srow[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        const uint32_t col = min(n0 + kGemvCols * ct + c, n - 1);
+        wrow[ct] = wp + (uint64_t)col * (k / 2);
+        srow[ct] = we + (uint64_t)col * (k / 16);
+    }
 
-    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    v4f acc[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     for (uint32_t p0 = s_begin; p0 < s_end; p0 += pass_steps) {
         const uint32_t plen = min(pass_steps, s_end - p0);
         // 1. activations of the pass: m rows of plen * 128 BF16, 1 KB copies
@@ -146,36 +156,44 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void w4a16_kernel(
         asm volatile("" ::: "memory");
         // 2. weights and scale codes, in the order the super-steps use them
         //    (clamped loads keep the code straight-line)
-        v4i wv[PS];
-        uint32_t sc[PS];
-        auto load_w = [&](int j) {
+        v4i wv[CT][PS];
+        uint32_t sc[CT][PS];
+        auto load_w = [&](int ct, int j) {
             const uint32_t kk = min((p0 + min((uint32_t)j, plen - 1)) * kStepK + 32 * q, k - 32);
-            wv[j] = *reinterpret_cast<const v4i *>(wrow + kk / 2);
+            wv[ct][j] = *reinterpret_cast<const v4i *>(wrow[ct] + kk / 2);
         };
         if constexpr (VS) {
             // 8 scale bytes per super-step: one 16-byte load per pair of super-steps;
             // the lane's two codes are bytes 8 j' + 2 q, i.e. dword 2 j' + q / 2
-            v4i sv[PS / 2];
+            v4i sv[CT][PS / 2];
 #pragma unroll
             for (int h = 0; h < PS / 2; ++h) {
                 const uint32_t g = min((p0 + 2 * h) * 8, k / 16 - 16);
-                sv[h] = *reinterpret_cast<const v4i *>(srow + g);
-                load_w(2 * h);
-                load_w(2 * h + 1);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    sv[ct][h] = *reinterpret_cast<const v4i *>(srow[ct] + g);
+                    load_w(ct, 2 * h);
+                    load_w(ct, 2 * h + 1);
+                }
             }
 #pragma unroll
-            for (int j = 0; j < PS; ++j) {
-                const uint32_t d0 = (j & 1) ? sv[j / 2].z : sv[j / 2].x;
-                const uint32_t d1 = (j & 1) ? sv[j / 2].w : sv[j / 2].y;
-                const uint32_t d = (q >> 1) ? d1 : d0;
-                sc[j] = (q & 1) ? d >> 16 : d & 0xFFFFu;
-            }
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int j = 0; j < PS; ++j) {
+                    const uint32_t d0 = (j & 1) ? sv[ct][j / 2].z : sv[ct][j / 2].x;
+                    const uint32_t d1 = (j & 1) ? sv[ct][j / 2].w : sv[ct][j / 2].y;
+                    const uint32_t d = (q >> 1) ? d1 : d0;
+                    sc[ct][j] = (q & 1) ? d >> 16 : d & 0xFFFFu;
+                }
         } else {
 #pragma unroll
             for (int j = 0; j < PS; ++j) {
                 const uint32_t g = min(((p0 + min((uint32_t)j, plen - 1)) * kStepK + 32 * q) / 16, k / 16 - 2);
-                sc[j] = *reinterpret_cast<const uint16_t *>(srow + g);
-                load_w(j);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    sc[ct][j] = *reinterpret_cast<const uint16_t *>(srow[ct] + g);
+                    load_w(ct, j);
+                }
             }
         }
         asm volatile("" ::: "memory");
@@ -183,22 +201,44 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void w4a16_kernel(
         //    until only this pass's weight and scale loads may be outstanding
         //    means the activations are in LDS (the compiler then waits per
         //    super-step for just the loads that super-step reads)
-        wait_vm_le<VS ? PS + PS / 2 : 2 * PS>();
+        wait_vm_le<CT * (VS ? PS + PS / 2 : 2 * PS)>();
 
         const int8_t *xa = la + arow * pitch + 64 * q;  // this lane's 32 BF16 of a super-step
 #pragma unroll
         for (int j = 0; j < PS; ++j) {
             if ((uint32_t)j >= plen) break;
             const bool live = (p0 + j) * kStepK + 32 * q < k;  // quarters past K contribute 0
-            const ByteTable t0 = make_table(sc[j] & 0xFFu), t1 = make_table(sc[j] >> 8);
-            const uint32_t wd[4] = {(uint32_t)wv[j].x, (uint32_t)wv[j].y, (uint32_t)wv[j].z, (uint32_t)wv[j].w};
+            if constexpr (CT == 1) {
+                const ByteTable t0 = make_table(sc[0][j] & 0xFFu), t1 = make_table(sc[0][j] >> 8);
+                const uint32_t wd[4] = {(uint32_t)wv[0][j].x, (uint32_t)wv[0][j].y, (uint32_t)wv[0][j].z,
+                                        (uint32_t)wv[0][j].w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const v4i b = decode8(wd[t], t < 2 ? t0 : t1);
+                    v4i a = *reinterpret_cast<const v4i *>(xa + j * (kStepK * 2) + 16 * t);
+                    if (!live) a = v4i{0, 0, 0, 0};
+                    acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                     __builtin_bit_cast(bf16x8, b), acc[0], 0, 0, 0);
+                }
+                continue;
+            }
+            v4i a[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const v4i b = decode8(wd[t], t < 2 ? t0 : t1);
-                v4i a = *reinterpret_cast<const v4i *>(xa + j * (kStepK * 2) + 16 * t);
-                if (!live) a = v4i{0, 0, 0, 0};
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                              __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+                a[t] = *reinterpret_cast<const v4i *>(xa + j * (kStepK * 2) + 16 * t);
+                if (!live) a[t] = v4i{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const ByteTable t0 = make_table(sc[ct][j] & 0xFFu), t1 = make_table(sc[ct][j] >> 8);
+                const uint32_t wd[4] = {(uint32_t)wv[ct][j].x, (uint32_t)wv[ct][j].y, (uint32_t)wv[ct][j].z,
+                                        (uint32_t)wv[ct][j].w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const v4i b = decode8(wd[t], t < 2 ? t0 : t1);
+                    acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[t]),
+                                                                      __builtin_bit_cast(bf16x8, b), acc[ct], 0, 0, 0);
+                }
             }
         }
         asm volatile("" ::: "memory");  // the next pass's copies overwrite this pass's activations
@@ -208,14 +248,17 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void w4a16_kernel(
     __syncthreads();
     float *red = reinterpret_cast<float *>(smem);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[(wave * 64 + lane) * 4 + r] = acc[r];
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[((ct * kGemvMaxWaves + wave) * 64 + lane) * 4 + r] = acc[ct][r];
     __syncthreads();
-    if (wave == 0 && lane < 32) {
+    if (wave < CT && lane < 32) {
+        const int ct = wave;
         float tot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int v = 0; v < nwaves; ++v)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) tot[r] += red[(v * 64 + lane) * 4 + r];
-        const uint32_t oc = n0 + c;
+            for (int r = 0; r < 4; ++r) tot[r] += red[((ct * kGemvMaxWaves + v) * 64 + lane) * 4 + r];
+        const uint32_t oc = n0 + kGemvCols * ct + c;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const uint32_t row = 4 * q + r;
@@ -228,41 +271,58 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void w4a16_kernel(
 
 hipError_t launch_w4a16(const uint16_t *x, const uint8_t *w_packed, const uint8_t *w_e4m3, float scale2,
                         uint16_t *out, uint32_t m, uint32_t n, uint32_t k, hipStream_t s) {
-    // Waves per workgroup as for the int8 GEMV (~24 waves per CU over the
-    // launch), at most 16, at least enough for passes of kW4PassSteps; then
-    // the smallest number of passes whose activation staging fits in LDS.
-    const uint32_t tiles = (uint32_t)div_up(n, kGemvCols);
+    // Column tiles per workgroup: two from m = 4 on, where the activation
+    // bytes a workgroup stages (2 m per K element) approach the weight bytes
+    // of one 16-column tile (9 per K element) -- if that still leaves a
+    // workgroup for every CU.  Waves per workgroup as for the
+    // int8 GEMV (~24 waves per CU over the launch), at most 16 (and with two
+    // tiles, one of them reduces each tile's partial sums); then the smallest
+    // number of passes whose activation staging fits in LDS.
+    const uint32_t ct = m >= 4 && div_up(n, 2 * kGemvCols) >= (uint64_t)kGemmCus ? 2 : 1;
+    const uint32_t tiles = (uint32_t)div_up(n, kGemvCols * ct);
     const uint32_t nsteps = (uint32_t)div_up(k, kStepK);
     uint32_t waves = (uint32_t)div_up(6144, tiles);
-    waves = max(1u, min(waves, (uint32_t)kGemvMaxWaves));
-    waves = min(waves, nsteps);
+    waves = max(ct, min(waves, (uint32_t)kGemvMaxWaves));
+    waves = min(waves, max(nsteps, ct));
     const bool vs = k % 256 == 0;  // then nsteps is even
     uint32_t spw = (uint32_t)div_up(nsteps, waves);
     if (vs) spw += spw & 1u;  // even: every pass starts at an even super-step
-    waves = (uint32_t)div_up(nsteps, spw);
-    const uint32_t red = kGemvMaxWaves * 64 * 4 * 4;
+    waves = max((uint32_t)div_up(nsteps, spw), ct);
+    const uint32_t red = ct * kGemvMaxWaves * 64 * 4 * 4;
     // pass length: the whole per-wave range when its staging fits in LDS,
     // else the largest that fits (even when the scales are read 16 bytes at a
     // time); launched with PS rounded up to an instantiated length
-    uint32_t pass = min(spw, (uint32_t)kW4PassSteps);
+    uint32_t pass = min(spw, ct == 2 ? 6u : (uint32_t)kW4PassSteps);  // two tiles: 6 keeps 128 VGPRs
     const uint32_t step = vs ? 2u : 1u;
     while (pass > step && (uint64_t)waves * m * w4_pitch(pass) > 160 * 1024) pass -= step;
     pass = vs ? max(2u, (pass + 1) & ~1u) : (pass <= 2 ? pass : (pass + 1) & ~1u);
     const uint32_t lds = max((uint32_t)(waves * m * w4_pitch(pass)), red);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
-#define BSR_W4_LAUNCH(V, P)                                                                            \
-    hipLaunchKernelGGL((w4a16_kernel<V, P>), dim3(tiles), dim3(64 * waves), lds, s, x, w_packed, w_e4m3, \
+#define BSR_W4_LAUNCH(V, P, C)                                                                            \
+    hipLaunchKernelGGL((w4a16_kernel<V, P, C>), dim3(tiles), dim3(64 * waves), lds, s, x, w_packed, w_e4m3, \
                        scale2, out, m, n, k, spw)
-    switch ((vs ? 16 : 0) + pass) {
-    case 16 + 8: BSR_W4_LAUNCH(true, 8); break;
-    case 16 + 6: BSR_W4_LAUNCH(true, 6); break;
-    case 16 + 4: BSR_W4_LAUNCH(true, 4); break;
-    case 16 + 2: BSR_W4_LAUNCH(true, 2); break;
-    case 8: BSR_W4_LAUNCH(false, 8); break;
-    case 6: BSR_W4_LAUNCH(false, 6); break;
-    case 4: BSR_W4_LAUNCH(false, 4); break;
-    case 2: BSR_W4_LAUNCH(false, 2); break;
-    default: BSR_W4_LAUNCH(false, 1); break;
+    if (ct == 2) {
+        switch ((vs ? 16 : 0) + pass) {
+        case 16 + 6: BSR_W4_LAUNCH(true, 6, 2); break;
+        case 16 + 4: BSR_W4_LAUNCH(true, 4, 2); break;
+        case 16 + 2: BSR_W4_LAUNCH(true, 2, 2); break;
+        case 6: BSR_W4_LAUNCH(false, 6, 2); break;
+        case 4: BSR_W4_LAUNCH(false, 4, 2); break;
+        case 2: BSR_W4_LAUNCH(false, 2, 2); break;
+        default: BSR_W4_LAUNCH(false, 1, 2); break;
+        }
+    } else {
+        switch ((vs ? 16 : 0) + pass) {
+        case 16 + 8: BSR_W4_LAUNCH(true, 8, 1); break;
+        case 16 + 6: BSR_W4_LAUNCH(true, 6, 1); break;
+        case 16 + 4: BSR_W4_LAUNCH(true, 4, 1); break;
+        case 16 + 2: BSR_W4_LAUNCH(true, 2, 1); break;
+        case 8: BSR_W4_LAUNCH(false, 8, 1); break;
+        case 6: BSR_W4_LAUNCH(false, 6, 1); break;
+        case 4: BSR_W4_LAUNCH(false, 4, 1); break;
+        case 2: BSR_W4_LAUNCH(false, 2, 1); break;
+        default: BSR_W4_LAUNCH(false, 1, 1); break;
+        }
     }
 #undef BSR_W4_LAUNCH
     return hipGetLastError();
