@@ -255,25 +255,26 @@ __global__ __launch_bounds__(64) void gemv_chain_kernel(
 constexpr int kChainChunkBlocks = 32;
 constexpr int kChainRowPitch = kChainChunkBlocks * 32 + 16;  // bytes; +16 spreads 16 rows over the banks
 constexpr int kChainSPitch = kChainChunkBlocks + 4;          // floats per scale row
-constexpr int kChainARows = kGemvMaxRows;
-constexpr int kChainSRows = kGemvCols + kChainARows;         // w_s rows, then a_s rows
-
+// ROWS: activation rows the ring holds (m <= ROWS): copies and LDS scale
+// with the rows actually used.
+template <int ROWS>
 struct ChainBuf {
+    static constexpr int kSRows = kGemvCols + ROWS;  // w_s rows, then a_s rows
     int8_t w[kGemvCols * kChainRowPitch];
-    int8_t a[kChainARows * kChainRowPitch];
-    float s[kChainSRows * kChainSPitch];
+    int8_t a[ROWS * kChainRowPitch];
+    float s[kSRows * kChainSPitch];
 };
 
 // Copies of one chunk issued by the wave: one 1 KB copy per weight and
 // activation row, the scale rows flattened into 16-byte copies (4-byte copies
 // for grouped activation scales, expanded to one per block).  Every copy
 // instruction has live lanes, so each one counts once in vmcnt.
-template <bool AGROUP>
+template <bool AGROUP, int ROWS>
 struct ChainCopies {
     static constexpr int kScale16 = AGROUP ? (kGemvCols * kChainSPitch + 255) / 256
-                                           : (kChainSRows * kChainSPitch + 255) / 256;
-    static constexpr int kScale4 = AGROUP ? (kChainARows * kChainSPitch + 63) / 64 : 0;
-    static constexpr int kTotal = kGemvCols + kChainARows + kScale16 + kScale4;
+                                           : ((kGemvCols + ROWS) * kChainSPitch + 255) / 256;
+    static constexpr int kScale4 = AGROUP ? (ROWS * kChainSPitch + 63) / 64 : 0;
+    static constexpr int kTotal = kGemvCols + ROWS + kScale16 + kScale4;
 };
 
 // Operands of one iteration (4 blocks) of the streamed chain kernel: per
@@ -286,13 +287,14 @@ struct ChainOps {
 };
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-template <bool AGROUP, int RING>
+template <bool AGROUP, int RING, int ROWS>
 __global__ __launch_bounds__(64) void gemv_chain_lds_kernel(
     const int8_t *__restrict__ a, const int8_t *w, const float *__restrict__ a_s,
     const float *__restrict__ w_s, uint16_t *__restrict__ out, uint32_t m, uint32_t n, uint32_t k,
     uint32_t a_ld, uint32_t a_shift) {
-    __shared__ __attribute__((aligned(16))) ChainBuf ring[RING];
-    constexpr int NC = ChainCopies<AGROUP>::kTotal;
+    using Buf = ChainBuf<ROWS>;
+    __shared__ __attribute__((aligned(16))) Buf ring[RING];
+    constexpr int NC = ChainCopies<AGROUP, ROWS>::kTotal;
     static_assert(NC * (RING - 1) < 64, "the copies in flight fit the vmcnt range");
 
     const int lane = threadIdx.x & 63;
@@ -303,7 +305,7 @@ __global__ __launch_bounds__(64) void gemv_chain_lds_kernel(
     const uint32_t nchunks = (nb + kChainChunkBlocks - 1) / kChainChunkBlocks;
 
     auto issue = [&](int bi, uint32_t chunk) {
-        ChainBuf &b = ring[bi];
+        Buf &b = ring[bi];
         // row bases are wave-uniform (scalar registers); lanes add a 32-bit offset
         const uint32_t off = min(chunk * (uint32_t)kChainChunkBlocks * 32 + 16 * lane, k - 16);
 #pragma unroll
@@ -312,14 +314,14 @@ __global__ __launch_bounds__(64) void gemv_chain_lds_kernel(
             __builtin_amdgcn_global_load_lds(row + off, (lds_void *)(b.w + r * kChainRowPitch), 16, 0, 0);
         }
 #pragma unroll
-        for (int r = 0; r < kChainARows; ++r) {
+        for (int r = 0; r < ROWS; ++r) {
             const int8_t *row = a + (uint64_t)min((uint32_t)r, m - 1) * k;
             __builtin_amdgcn_global_load_lds(row + off, (lds_void *)(b.a + r * kChainRowPitch), 16, 0, 0);
         }
         const uint32_t bb0 = chunk * kChainChunkBlocks;
-        constexpr uint32_t s_rows16 = AGROUP ? kGemvCols : kChainSRows;
+        constexpr uint32_t s_rows16 = AGROUP ? kGemvCols : Buf::kSRows;
 #pragma unroll
-        for (int i = 0; i < ChainCopies<AGROUP>::kScale16; ++i) {
+        for (int i = 0; i < ChainCopies<AGROUP, ROWS>::kScale16; ++i) {
             const uint32_t p = i * 256 + 4 * lane;  // float index in the region
             const uint32_t r = min(p / kChainSPitch, s_rows16 - 1);
             const uint32_t cb = min(bb0 + min(p % kChainSPitch, (uint32_t)kChainChunkBlocks - 4), nb - 4);
@@ -329,11 +331,11 @@ __global__ __launch_bounds__(64) void gemv_chain_lds_kernel(
                 __builtin_amdgcn_global_load_lds(src, (lds_void *)(b.s + i * 256), 16, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < ChainCopies<AGROUP>::kScale4; ++i) {
+        for (int i = 0; i < ChainCopies<AGROUP, ROWS>::kScale4; ++i) {
             const uint32_t p = i * 64 + lane;
-            const uint32_t r = min(p / kChainSPitch, (uint32_t)kChainARows - 1);
+            const uint32_t r = min(p / kChainSPitch, (uint32_t)ROWS - 1);
             const uint32_t cb = min(bb0 + min(p % kChainSPitch, (uint32_t)kChainChunkBlocks - 1), nb - 1);
-            if (p < kChainARows * kChainSPitch)
+            if (p < ROWS * kChainSPitch)
                 __builtin_amdgcn_global_load_lds(a_s + (uint64_t)min(r, m - 1) * a_ld + (cb >> a_shift),
                                                  (lds_void *)(b.s + kGemvCols * kChainSPitch + i * 64), 4, 0, 0);
         }
@@ -345,9 +347,9 @@ __global__ __launch_bounds__(64) void gemv_chain_lds_kernel(
     // iteration's arithmetic, which hides their latency.
     auto compute = [&](int bi, uint32_t chunk, auto full_chunk) {
         constexpr bool full = decltype(full_chunk)::value;
-        const ChainBuf &b = ring[bi];
+        const Buf &b = ring[bi];
         const int8_t *wr = b.w + c16 * kChainRowPitch + 8 * q;
-        const int8_t *ar = b.a + min(c16, (uint32_t)kChainARows - 1) * kChainRowPitch + 8 * q;
+        const int8_t *ar = b.a + min(c16, (uint32_t)ROWS - 1) * kChainRowPitch + 8 * q;
         const float *wsr = b.s + c16 * kChainSPitch + q;
         const float *asr = b.s + (kGemvCols + min(c16, m - 1)) * kChainSPitch + q;
         auto read = [&](ChainOps &x, int i) {
@@ -575,15 +577,26 @@ hipError_t launch_gemv_chain(const int8_t *a_i8, const int8_t *w_i8, const float
     if (nb % 4 == 0) {
         // few column tiles: one workgroup per CU, so a deeper ring costs nothing
         const bool deep = grid.x <= (uint32_t)kGemmCus;
-        if (a_shift)  // (its 32 copies per chunk allow one chunk in flight)
-            hipLaunchKernelGGL((gemv_chain_lds_kernel<true, 2>), grid, blk, 0, s, a_i8, w_i8, a_scale, w_scale,
-                               out, m, n, k, a_ld, a_shift);
-        else if (deep)
-            hipLaunchKernelGGL((gemv_chain_lds_kernel<false, 3>), grid, blk, 0, s, a_i8, w_i8, a_scale, w_scale,
-                               out, m, n, k, a_ld, a_shift);
-        else
-            hipLaunchKernelGGL((gemv_chain_lds_kernel<false, 2>), grid, blk, 0, s, a_i8, w_i8, a_scale, w_scale,
-                               out, m, n, k, a_ld, a_shift);
+        const uint32_t rows = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8;
+#define BSR_CHAIN(AG, RG, RW)                                                                              \
+    hipLaunchKernelGGL((gemv_chain_lds_kernel<AG, RG, RW>), grid, blk, 0, s, a_i8, w_i8, a_scale, w_scale, \
+                       out, m, n, k, a_ld, a_shift)
+#define BSR_CHAIN_ROWS(AG, RG)                  \
+    switch (rows) {                             \
+    case 1: BSR_CHAIN(AG, RG, 1); break;        \
+    case 2: BSR_CHAIN(AG, RG, 2); break;        \
+    case 4: BSR_CHAIN(AG, RG, 4); break;        \
+    default: BSR_CHAIN(AG, RG, 8); break;       \
+    }
+        if (a_shift) {  // (its copies per chunk allow one chunk in flight)
+            BSR_CHAIN_ROWS(true, 2)
+        } else if (deep) {
+            BSR_CHAIN_ROWS(false, 3)
+        } else {
+            BSR_CHAIN_ROWS(false, 2)
+        }
+#undef BSR_CHAIN_ROWS
+#undef BSR_CHAIN
         return hipGetLastError();
     }
     if (a_shift)
