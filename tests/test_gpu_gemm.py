@@ -273,3 +273,25 @@ def test_error_status_leaves_output_untouched():
     assert st == bsr.BSR_OK
     torch.cuda.synchronize()
     assert torch.all(raw[:m * n] == 0) and torch.all(raw[m * n:] == 0x1234)
+
+
+@pytest.mark.parametrize("m,k,path", [(300, 1024, bsr.PATH_GEMM), (4, 4096, bsr.PATH_GEMV),
+                                      (8, 16384, bsr.PATH_GEMV), (3, 1056, bsr.PATH_GEMV),
+                                      (5, 4096, bsr.PATH_INVARIANT), (2, 1056, bsr.PATH_INVARIANT)])
+def test_scales_at_4_byte_alignment(m, k, path):
+    """The ABI asks only 4-byte alignment of the F32 scales: scale tensors that
+    start one float into their allocation give the same bits."""
+    n = 96
+    say(f"4-byte-aligned scales m={m} k={k} path={path}")
+    a, w, a_s, w_s = _rand_operands(7 + m + k, m, n, k)
+    da, dw = to_dev(a), to_dev(w)
+    ref = host(gpu_gemm(da, dw, to_dev(a_s), to_dev(w_s), path=path))
+    big_a = torch.zeros(a_s.size + 4, dtype=torch.float32, device=DEV)
+    big_w = torch.zeros(w_s.size + 4, dtype=torch.float32, device=DEV)
+    sa = big_a[1:1 + a_s.size].view(a_s.shape)
+    sw = big_w[1:1 + w_s.size].view(w_s.shape)
+    sa.copy_(to_dev(a_s))
+    sw.copy_(to_dev(w_s))
+    assert sa.data_ptr() % 16 == 4 and sw.data_ptr() % 16 == 4
+    out = host(gpu_gemm(da, dw, sa, sw, path=path))
+    assert np.array_equal(out, ref)
