@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "int8 block-scaled GEMM TOPS (prefill) + GEMV HBM GB/s, % of MI355X peak"
 PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA
+PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12   # non-packed FP32 VALU lane operations per second (T)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -383,6 +384,15 @@ def main():
                             "unit": "TOPS", "frac": g["tops"] / PEAK_INT8_TOPS,
                             "traffic": _traffic("gemm_kernel", ["gemm.hip", "bsr_internal.h"], None),
                             "kernel": "gemm_kernel (int8_gemm_blockscaled, m > 8)"}
+        # The same kernel against the vector ALU, which bounds it: the exact
+        # per-block FP32 rescale is one int32 -> FP32 conversion and one FMA per
+        # output and 32-wide K block; peak = 256 CUs x 4 SIMDs x 16 lanes x
+        # 2.4 GHz non-packed FP32 lane operations.
+        alu_ops = 2.0 * M * N * (K // 32)
+        alu = alu_ops / (g["us_in_step_mean"] * 1e-6) / 1e12
+        line["roofline_alu"] = {"bound": "alu", "achieved": alu, "peak": PEAK_VALU_TOPS,
+                                "unit": "T lane-ops/s", "frac": alu / PEAK_VALU_TOPS,
+                                "work": "int32->FP32 conversion + FMA per output and K block"}
         line["kernels"] = pre["kernels"]
         line["parity"] = pre["parity_sampled_rows"]
     if cpu:
