@@ -18,16 +18,19 @@
 // exactly.  Output lane l holds column l % 16, rows 4 * (l / 16) + r (r < 4),
 // so lanes 0-31 hold all m <= 8 rows.
 //
-// Two kernels share that arithmetic:
+// Kernels:
 //  * staged: the workgroup first copies its activations, activation scales
 //    and the scales of its 16 weight rows into LDS (global_load_lds), so the
 //    only global loads of the K loop are weight bytes -- one 1 KB instruction
 //    per wave step;
 //  * direct: every operand comes from global memory.  Used when the staged
 //    copies do not fit in LDS or K is not a multiple of 128;
-//  * chain: one wave per workgroup runs all of K in block order, so each
-//    output is the same FP32 chain acc = fma(P_b, fl32(a_s * w_s), acc),
-//    b = 0, 1, ..., that the GEMM evaluates -- its BF16 bits equal the GEMM's.
+//  * chain (the path-invariant GEMV): one wave per workgroup runs all of K in
+//    block order, so each output is the same FP32 chain
+//    acc = fma(P_b, fl32(a_s * w_s), acc), b = 0, 1, ..., that the GEMM
+//    evaluates -- its BF16 bits equal the GEMM's.  The streamed form
+//    (K % 128 == 0) brings every operand through an LDS ring and takes K = 32
+//    MFMAs; the register form is the fallback.
 #include <type_traits>
 
 #include "bsr_internal.h"
