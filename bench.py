@@ -383,7 +383,7 @@ def main():
         line["roofline"] = {"bound": "mfma", "achieved": g["tops"], "peak": PEAK_INT8_TOPS,
                             "unit": "TOPS", "frac": g["tops"] / PEAK_INT8_TOPS,
                             "traffic": _traffic("gemm_kernel", ["gemm.hip", "bsr_internal.h"], None),
-                            "kernel": "gemm_kernel (int8_gemm_blockscaled, m > 8)"}
+                            "kernel": "gemm_kernel (int8_gemm_blockscaled, m > 16)"}
         # The same kernel against the vector ALU, which bounds it: the exact
         # per-block FP32 rescale is one int32 -> FP32 conversion and one FMA per
         # output and 32-wide K block; peak = 256 CUs x 4 SIMDs x 16 lanes x

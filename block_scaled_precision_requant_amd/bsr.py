@@ -130,7 +130,7 @@ def silu_mul_requant_int8(gate, up, a_i8, a_scale, stream=None):
 
 
 def w4a16_gemv(x_bf16, w_packed, w_e4m3, scale2, out, stream=None):
-    """out [M,N] BF16 = x_bf16 [M,K] (M <= 8) times the NVFP4 weight (w_packed [N,K/2] u8,
+    """out [M,N] BF16 = x_bf16 [M,K] (M <= 16) times the NVFP4 weight (w_packed [N,K/2] u8,
     w_e4m3 [N,K/16] u8, scale2), dequantized on the fly."""
     m, k = x_bf16.shape
     n = w_packed.shape[0]
@@ -158,7 +158,7 @@ def int8_gemm_blockscaled_ex(a_i8, w_i8, a_scale, w_scale, out, path=PATH_AUTO, 
 
 
 def int8_gemm_blockscaled(a_i8, w_i8, a_scale, w_scale, out, stream=None):
-    """As int8_gemm_blockscaled_ex with the automatic path (GEMV iff M <= 8)."""
+    """As int8_gemm_blockscaled_ex with the automatic path (GEMV iff M <= 16)."""
     m, k = a_i8.shape
     n = w_i8.shape[0]
     _shape(a_i8, (m, k), "a_i8")

@@ -1,4 +1,4 @@
-// api.hip -- the C ABI of libbsr: argument validation, the m <= 8 dispatch
+// api.hip -- the C ABI of libbsr: argument validation, the m <= 16 dispatch
 // and the launches.  Every check happens before the first launch; an error
 // launches nothing.  The only state is a per-device cache of the gfx950 check.
 #include <atomic>

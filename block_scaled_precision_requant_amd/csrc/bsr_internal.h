@@ -21,7 +21,7 @@ constexpr int kRqwUnroll = 2;        // blocks per lane, loads issued together
 constexpr int kSiluUnroll = 2;       // chunks per lane and pass of the SiLU table kernel
 constexpr int kSiluThreads = 512;    // lanes per workgroup of the SiLU table kernel
 
-// ---- GEMM (m > 8) ---------------------------------------------------------
+// ---- GEMM (m > 16) --------------------------------------------------------
 // A workgroup computes a BM x BN output tile; each wave owns a WM x WN piece
 // made of 32 x 32 MFMA tiles.  The K loop stages kGemmStageBlocks 32-wide
 // blocks of A, W and their scales per LDS buffer, in a ring of kGemmRing
@@ -38,7 +38,7 @@ constexpr int kGemmGroupM = 8;
 constexpr int kXcds = 8;
 constexpr int kGemmCus = 256;                             // compute units of an MI355X
 
-// ---- GEMV (m <= 8) --------------------------------------------------------
+// ---- GEMV (m <= 16) -------------------------------------------------------
 // A workgroup owns kGemvCols output columns and splits K over its waves; each
 // wave runs v_mfma_i32_16x16x64_i8 on (activation rows padded to 16) x (16
 // weight rows), one 64-byte K step at a time, the two 32-wide blocks of a step
@@ -46,10 +46,10 @@ constexpr int kGemmCus = 256;                             // compute units of an
 // partial sums are added in LDS in a fixed order.
 constexpr int kGemvCols = 16;
 constexpr int kGemvMaxWaves = 16;
-constexpr int kGemvMaxRows = 8;
+constexpr int kGemvMaxRows = 16;  // the rows of one 16x16 MFMA output tile
 constexpr int kGemvBlocksPerIter = 4;   // K blocks per loop iteration of a wave (two MFMA steps)
 
-// ---- W4A16 decode GEMV (m <= 8, straight from NVFP4) ------------------------
+// ---- W4A16 decode GEMV (m <= 16, straight from NVFP4) -----------------------
 // Same workgroup shape as the int8 GEMV; K in super-steps of 128, at most
 // kW4PassSteps per staging pass of a wave.
 constexpr int kW4PassSteps = 8;

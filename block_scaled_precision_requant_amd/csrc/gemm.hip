@@ -1,4 +1,4 @@
-// gemm.hip -- int8 x int8 block-scaled GEMM for gfx950 (m > 8).
+// gemm.hip -- int8 x int8 block-scaled GEMM for gfx950 (m > 16).
 //
 // Computes out[i,j] = bf16_rne( sum_b fl32(a_s[i,b] * w_s[j,b]) * P[i,j,b] ) with
 // P the exact int32 dot product of 32-wide K block b -- the second launch of

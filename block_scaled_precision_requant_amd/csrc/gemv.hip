@@ -1,4 +1,4 @@
-// gemv.hip -- weight-streaming block-scaled GEMV for gfx950 (m <= 8).
+// gemv.hip -- weight-streaming block-scaled GEMV for gfx950 (m <= 16).
 //
 // Same result definition as the GEMM (page "metrale_model_layers/layers/ops/
 // gemm_dense_int8.rs", second launch of `int8_gemm_faith2_prefill`): exact
@@ -15,8 +15,8 @@
 // offset.  One v_mfma_i32_16x16x64_i8 with the activation quarters 2-3 zeroed
 // gives the first block's P, one with quarters 0-1 zeroed the second's: lanes
 // pair A and B bytes by (quarter, byte), so the zeroed quarters drop out
-// exactly.  Output lane l holds column l % 16, rows 4 * (l / 16) + r (r < 4),
-// so lanes 0-31 hold all m <= 8 rows.
+// exactly.  Output lane l holds column l % 16, rows 4 * (l / 16) + r (r < 4):
+// the 16 rows of the MFMA cover m <= 16 at no extra matrix-core cost.
 //
 // Kernels:
 //  * staged: the workgroup first copies its activations, activation scales
@@ -83,7 +83,7 @@ __device__ __forceinline__ void gemv_reduce_store(float *red, const float (&acc)
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[(wave * 64 + lane) * 4 + r] = acc[r];
     __syncthreads();
-    if (wave == 0 && lane < 32) {
+    if (wave == 0) {
         float tot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int v = 0; v < nwaves; ++v)
 #pragma unroll
@@ -580,7 +580,7 @@ hipError_t launch_gemv_chain(const int8_t *a_i8, const int8_t *w_i8, const float
     if (nb % 4 == 0) {
         // few column tiles: one workgroup per CU, so a deeper ring costs nothing
         const bool deep = grid.x <= (uint32_t)kGemmCus;
-        const uint32_t rows = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8;
+        const uint32_t rows = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : m <= 8 ? 8 : 16;
 #define BSR_CHAIN(AG, RG, RW)                                                                              \
     hipLaunchKernelGGL((gemv_chain_lds_kernel<AG, RG, RW>), grid, blk, 0, s, a_i8, w_i8, a_scale, w_scale, \
                        out, m, n, k, a_ld, a_shift)
@@ -591,7 +591,10 @@ hipError_t launch_gemv_chain(const int8_t *a_i8, const int8_t *w_i8, const float
     case 4: BSR_CHAIN(AG, RG, 4); break;        \
     default: BSR_CHAIN(AG, RG, 8); break;       \
     }
-        if (a_shift) {  // (its copies per chunk allow one chunk in flight)
+        if (rows == 16) {  // (37 or 44 copies per chunk: one chunk in flight)
+            if (a_shift) BSR_CHAIN(true, 2, 16);
+            else BSR_CHAIN(false, 2, 16);
+        } else if (a_shift) {  // (its copies per chunk allow one chunk in flight)
             BSR_CHAIN_ROWS(true, 2)
         } else if (deep) {
             BSR_CHAIN_ROWS(false, 3)

@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void w4a16_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) red[((ct * kGemvMaxWaves + wave) * 64 + lane) * 4 + r] = acc[ct][r];
     __syncthreads();
-    if (wave < CT && lane < 32) {
+    if (wave < CT) {
         const int ct = wave;
         float tot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int v = 0; v < nwaves; ++v)

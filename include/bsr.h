@@ -8,7 +8,7 @@
  *   3. int8_gemm_blockscaled -- int8 x int8 with an exact int32 dot product per
  *      32-wide K block, each block rescaled in FP32 by a_scale * w_scale,
  *      accumulated in FP32 and written as BF16 (an MFMA GEMM for M > 8, a
- *      weight-streaming GEMV for M <= 8).
+ *      weight-streaming GEMV for M <= 16).
  * The operations are those of page "metrale_model_layers/layers/ops/
  * gemm_dense_int8.rs": the doc comments of `requant_w_nvfp4_int8` and
  * `int8_gemm_faith2_prefill` (the latter's two launches are entry points 2
@@ -102,7 +102,8 @@ int requant_a_int8(const uint16_t *a_bf16, int8_t *a_i8, float *a_scale,
  * summation order is the kernel's own (not part of the contract); the result
  * is within 4e-3 relative or 1 BF16 ulp of the FP64 value, or within the
  * worst-case FP32 error of a K/32-term sum where that is larger.
- * m <= 8 runs the weight-streaming GEMV, m > 8 the MFMA GEMM.
+ * m <= 16 (one 16-row matrix-core tile) runs the weight-streaming GEMV, m > 16
+ * the MFMA GEMM.
  * Errors: BSR_EINVAL, BSR_ENULL, BSR_EALIGN, BSR_EDEVICE, BSR_ELAUNCH.
  */
 int int8_gemm_blockscaled(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
@@ -111,12 +112,12 @@ int int8_gemm_blockscaled(const int8_t *a_i8, const int8_t *w_i8, const float *a
 
 /* Paths of int8_gemm_blockscaled_ex. */
 enum bsr_path {
-    BSR_PATH_AUTO = 0, /* GEMV iff m <= 8, as int8_gemm_blockscaled     */
+    BSR_PATH_AUTO = 0, /* GEMV iff m <= 16, as int8_gemm_blockscaled    */
     BSR_PATH_GEMM = 1, /* the MFMA GEMM at any m                         */
-    BSR_PATH_GEMV = 2, /* the GEMV; requires m <= 8, else BSR_EINVAL     */
-    BSR_PATH_INVARIANT = 3 /* m <= 8: a GEMV that accumulates every output
+    BSR_PATH_GEMV = 2, /* the GEMV; requires m <= 16, else BSR_EINVAL    */
+    BSR_PATH_INVARIANT = 3 /* m <= 16: a GEMV that accumulates every output
                             * over the K blocks in increasing order, as the
-                            * GEMM does; m > 8: the GEMM.  A row's output
+                            * GEMM does; m > 16: the GEMM.  A row's output
                             * bits then depend on neither m nor the path
                             * (the invariants stated for `W8a8Weight::segment`
                             * on page "metrale_model_layers/layers/ops/
@@ -159,7 +160,7 @@ int silu_mul_requant_int8(const uint16_t *gate, const uint16_t *up, uint32_t ld,
  * W4A16 decode GEMV straight from the NVFP4 weight, no int8 requant (the
  * decode launcher of page "metrale_model_layers/layers/ops/gemv_sw.rs":
  * BF16 input, packed weight, E4M3 weight scale, F32 scale_2, BF16 output).
- *   x_bf16   [m, k]    BF16 as raw u16, 16-byte aligned, 1 <= m <= 8
+ *   x_bf16   [m, k]    BF16 as raw u16, 16-byte aligned, 1 <= m <= 16
  *   w_packed [n, k/2]  u8 (E2M1 pairs, low nibble first), 16-byte aligned
  *   w_e4m3   [n, k/16] u8, 16-byte aligned when k % 256 == 0, else 2-byte
  *   out      [m, n]    BF16 as raw u16, 2-byte aligned
@@ -167,7 +168,7 @@ int silu_mul_requant_int8(const uint16_t *gate, const uint16_t *up, uint32_t ld,
  * x[i,k] * e2m1[j,k] * s16[j,k/16] (each product exact; the summation order
  * is the kernel's own): within 4e-3 relative or 1 BF16 ulp of the FP64 value,
  * or within the worst-case FP32 error of a (k + 16)-term sum.
- * Errors: BSR_EINVAL (k, m > 8, scale2 not finite), BSR_ENULL, BSR_EALIGN,
+ * Errors: BSR_EINVAL (k, m > 16, scale2 not finite), BSR_ENULL, BSR_EALIGN,
  * BSR_EDEVICE, BSR_ELAUNCH.
  */
 int w4a16_gemv(const uint16_t *x_bf16, const uint8_t *w_packed, const uint8_t *w_e4m3, float scale2,

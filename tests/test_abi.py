@@ -92,7 +92,7 @@ def test_silu_requant_validation():
 def test_w4a16_validation():
     L = bsr.lib()
     null = ctypes.c_void_p(0)
-    assert L.w4a16_gemv(FAKE, FAKE, FAKE, 1.0, FAKE, 9, 4, 256, None) == bsr.BSR_EINVAL    # m > 8
+    assert L.w4a16_gemv(FAKE, FAKE, FAKE, 1.0, FAKE, 17, 4, 256, None) == bsr.BSR_EINVAL   # m > 16
     assert L.w4a16_gemv(FAKE, FAKE, FAKE, 1.0, FAKE, 1, 4, 48, None) == bsr.BSR_EINVAL     # k
     assert L.w4a16_gemv(FAKE, FAKE, FAKE, float("nan"), FAKE, 1, 4, 256, None) == bsr.BSR_EINVAL
     assert L.w4a16_gemv(FAKE, FAKE, FAKE, 1.0, FAKE, 0, 4, 256, None) == bsr.BSR_OK
@@ -107,7 +107,7 @@ def test_bad_scale2_and_path():
         assert L.requant_w_nvfp4_int8(FAKE, FAKE, s2, FAKE, FAKE, 4, 64, None) == bsr.BSR_EINVAL
     assert L.int8_gemm_blockscaled_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 64, None, 4) == bsr.BSR_EINVAL
     assert L.int8_gemm_blockscaled_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 64, None, -1) == bsr.BSR_EINVAL
-    assert L.int8_gemm_blockscaled_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 9, 4, 64, None,
+    assert L.int8_gemm_blockscaled_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 17, 4, 64, None,
                                       bsr.PATH_GEMV) == bsr.BSR_EINVAL
 
 
@@ -136,7 +136,7 @@ def test_gemm_agroup_validation():
     assert L.int8_gemm_blockscaled_agroup(*args, 64, FAKE, FAKE, 4, 4, 128, None, 0) == bsr.BSR_EINVAL
     assert L.int8_gemm_blockscaled_agroup(*args, 128, FAKE, FAKE, 4, 4, 96, None, 0) == bsr.BSR_EINVAL
     assert L.int8_gemm_blockscaled_agroup(*args, 0, FAKE, FAKE, 4, 4, 48, None, 0) == bsr.BSR_EINVAL
-    assert L.int8_gemm_blockscaled_agroup(*args, 0, FAKE, FAKE, 9, 4, 96, None, 2) == bsr.BSR_EINVAL  # gemv m>8
+    assert L.int8_gemm_blockscaled_agroup(*args, 0, FAKE, FAKE, 17, 4, 96, None, 2) == bsr.BSR_EINVAL  # gemv m>16
     assert L.int8_gemm_blockscaled_agroup(*args, 0, FAKE, FAKE, 4, 4, 96, None, 7) == bsr.BSR_EINVAL  # path
     assert L.int8_gemm_blockscaled_agroup(*args, 128, FAKE, FAKE, 0, 4, 256, None, 0) == bsr.BSR_OK
     assert L.int8_gemm_blockscaled_agroup(FAKE, FAKE, None, 128, FAKE, FAKE, 4, 4, 256, None, 0) == bsr.BSR_ENULL

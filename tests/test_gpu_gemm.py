@@ -51,14 +51,15 @@ def test_gemm_parity_random(m, n, k):
 # vector scale loads runs, while m = 1 at that K is staged.
 @pytest.mark.parametrize("m,k", [(1, 1056), (2, 1056), (3, 1056), (4, 1056), (5, 1056), (6, 1056),
                                  (7, 1056), (8, 1056), (2, 2400), (1, 2176), (3, 2176), (8, 2176),
-                                 (5, 4096), (8, 4096), (1, 16384), (8, 16384)])
+                                 (5, 4096), (8, 4096), (1, 16384), (8, 16384), (9, 1056), (12, 2176),
+                                 (13, 2400), (16, 4096), (16, 16384), (11, 14336)])
 def test_gemv_parity_random_and_against_gemm(m, k):
     n = 333
     say(f"gemv m={m} n={n} k={k}")
     a, w, a_s, w_s = _rand_operands(100 + m, m, n, k, zero_frac=0.05)
     y, t = oracle.gemm_ref(a, w, a_s, w_s)
     da, dw, das, dws = to_dev(a), to_dev(w), to_dev(a_s), to_dev(w_s)
-    out_v = host(gpu_gemm(da, dw, das, dws, path=bsr.PATH_AUTO))     # m <= 8 -> GEMV
+    out_v = host(gpu_gemm(da, dw, das, dws, path=bsr.PATH_AUTO))     # m <= 16 -> GEMV
     out_g = host(gpu_gemm(da, dw, das, dws, path=bsr.PATH_GEMM))
     _check(f"gemv m={m}", out_v, y, t, k)
     _check(f"gemm m={m}", out_g, y, t, k)

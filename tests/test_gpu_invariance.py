@@ -1,5 +1,5 @@
 """Path and batch invariance on the GPU: with BSR_PATH_INVARIANT a row's BF16
-bits do not depend on m or on which kernel ran.  For m <= 8 that path runs the
+bits do not depend on m or on which kernel ran.  For m <= 16 that path runs the
 chain GEMV, which accumulates every output over the K blocks in increasing
 order exactly as the GEMM does, so its output must equal the GEMM path's bit
 for bit -- and both stay within the oracle's tolerance."""
@@ -24,7 +24,7 @@ def _operands(seed, m, n, k):
 
 
 @pytest.mark.parametrize("k", [32, 96, 1056, 4096, 14336])
-@pytest.mark.parametrize("m", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8, 9, 16])
 def test_invariant_gemv_equals_gemm(m, k):
     n = 200
     say(f"invariant gemv m={m} n={n} k={k}")
@@ -42,13 +42,14 @@ def test_invariant_gemv_equals_gemm(m, k):
 
 
 def test_invariant_rows_independent_of_m():
-    """Rows of a 300-row GEMM equal the same rows run alone or in groups of up to 8."""
+    """Rows of a 300-row GEMM equal the same rows run alone or in groups of up to 16."""
     m, n, k = 300, 333, 2048
     a, packed, e4m3 = _operands(5, m, n, k)
     w_i8, w_s = gpu_requant_w(packed, e4m3, inputs.SCALE2_1_448)
     a_i8, a_s = gpu_requant_a(a)
     full = host(gpu_gemm(a_i8, w_i8, a_s, w_s, path=bsr.PATH_INVARIANT))
-    for lo, hi in [(0, 1), (7, 15), (100, 103), (299, 300), (42, 48), (150, 159), (10, 140)]:
+    for lo, hi in [(0, 1), (7, 15), (100, 103), (299, 300), (42, 48), (150, 159), (10, 140), (20, 36),
+                   (283, 295)]:
         part = host(gpu_gemm(a_i8[lo:hi].contiguous(), w_i8, a_s[lo:hi].contiguous(), w_s,
                              path=bsr.PATH_INVARIANT))
         assert np.array_equal(part, full[lo:hi]), (lo, hi)
@@ -68,7 +69,7 @@ def test_invariant_decode_workloads(name):
 
 
 @pytest.mark.parametrize("group", [128, 0])
-@pytest.mark.parametrize("m", [1, 8])
+@pytest.mark.parametrize("m", [1, 8, 16])
 def test_invariant_grouped_scales(m, group):
     n, k = 130, 4096
     a, packed, e4m3 = _operands(77 + m, m, n, k)

@@ -32,7 +32,8 @@ def _weight(rng, n, k, general=True):
 # K % 256 == 0 -> 16-byte scale loads; other K -> per-step 2-byte loads, and
 # K % 128 != 0 leaves a partial last super-step.
 @pytest.mark.parametrize("m,n,k", [(1, 333, 256), (2, 70, 2048), (8, 129, 4096), (3, 333, 1056),
-                                   (5, 40, 96), (7, 16, 4128), (4, 1, 512), (8, 300, 14336)])
+                                   (5, 40, 96), (7, 16, 4128), (4, 1, 512), (8, 300, 14336),
+                                   (16, 600, 4096), (12, 300, 14336), (9, 70, 1056)])
 def test_random_shapes(m, n, k):
     rng = np.random.default_rng(m * 7919 + n * 31 + k)
     x = inputs.bf16_normal(rng, m, k)
@@ -83,7 +84,7 @@ def test_errors_launch_nothing():
     we = torch.zeros((4, 16), dtype=torch.uint8, device=DEV)
     out = torch.full((9, 4), 3, dtype=torch.int16, device=DEV)
     args = lambda m, k, e=we.data_ptr(): (x.data_ptr(), wp.data_ptr(), e, 1.0, out.data_ptr(), m, 4, k, None)
-    assert L.w4a16_gemv(*args(9, 256)) == bsr.BSR_EINVAL          # m > 8
+    assert L.w4a16_gemv(*args(17, 256)) == bsr.BSR_EINVAL         # m > 16
     assert L.w4a16_gemv(*args(1, 48)) == bsr.BSR_EINVAL           # k
     assert L.w4a16_gemv(*args(1, 256, we.data_ptr() + 2)) == bsr.BSR_EALIGN
     assert L.w4a16_gemv(x.data_ptr(), wp.data_ptr(), we.data_ptr(), float("inf"), out.data_ptr(), 1, 4, 256,
