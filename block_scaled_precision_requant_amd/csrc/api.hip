@@ -48,7 +48,7 @@ int gemm_args_check(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale
     if (!aligned(a_i8, 16) || !aligned(w_i8, 16) || !aligned(a_scale, 4) || !aligned(w_scale, 4) ||
         !aligned(out, 2))
         return BSR_EALIGN;
-    const uint64_t tiles = bsr::div_up(m, bsr::kGemmBMSmall) * bsr::div_up(n, bsr::kGemmBN);
+    const uint64_t tiles = bsr::div_up(m, bsr::kGemmSmallTile) * bsr::div_up(n, bsr::kGemmSmallTile);
     if (tiles > kMaxGrid) return BSR_EINVAL;
     return BSR_OK;
 }

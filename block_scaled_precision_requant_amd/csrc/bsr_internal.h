@@ -26,11 +26,13 @@ constexpr int kSiluThreads = 512;    // lanes per workgroup of the SiLU table ke
 // made of 32 x 32 MFMA tiles.  The K loop stages kGemmStageBlocks 32-wide
 // blocks of A, W and their scales per LDS buffer, in a ring of kGemmRing
 // buffers.  Workgroups are ordered so that each XCD runs a compact
-// kGemmGroupM-tall group of output tiles.  Two shapes are built, both 128 x
-// 128: sixteen 32 x 32 waves (m <= 128), and four 64 x 64 waves with two
-// workgroups per CU (m > 128).
-constexpr int kGemmBMSmall = 128;
+// kGemmGroupM-tall group of output tiles.  Two shapes are built: 128 x 128
+// with four 64 x 64 waves, and 64 x 64 with four 32 x 32 waves for grids of
+// the large tile too small to give every CU two workgroups; both run two
+// workgroups per CU.
+constexpr int kGemmBM = 128;
 constexpr int kGemmBN = 128;
+constexpr int kGemmSmallTile = 64;
 constexpr int kGemmStageBlocks = 4;
 constexpr int kGemmStageBytes = 32 * kGemmStageBlocks;    // 128 bytes of K per row: whole cache lines
 constexpr int kGemmRing = 2;                              // stage buffers in flight

@@ -112,3 +112,17 @@ def test_invariant_path_errors():
     bsr.int8_gemm_blockscaled_ex(a, w, s_a, s_w, out, path=bsr.PATH_INVARIANT)
     torch.cuda.synchronize()
     assert torch.all(out == 0)
+
+
+def test_rows_equal_across_gemm_tile_shapes():
+    """A 2048-row GEMM at N = 4096 runs 128x128 tiles; 100 of its rows alone run
+    64x64 tiles, and 16 of them the chain GEMV: the same bits every time."""
+    m, n, k = 2048, 4096, 512
+    a, packed, e4m3 = _operands(11, m, n, k)
+    w_i8, w_s = gpu_requant_w(packed, e4m3, inputs.SCALE2_1_448)
+    a_i8, a_s = gpu_requant_a(a)
+    full = host(gpu_gemm(a_i8, w_i8, a_s, w_s, path=bsr.PATH_INVARIANT))
+    for lo, hi in [(5, 105), (1000, 1016), (1900, 2048)]:
+        part = host(gpu_gemm(a_i8[lo:hi].contiguous(), w_i8, a_s[lo:hi].contiguous(), w_s,
+                             path=bsr.PATH_INVARIANT))
+        assert np.array_equal(part, full[lo:hi]), (lo, hi)
