@@ -120,7 +120,8 @@ int gemm_launch(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, ui
         return launched(bsr::launch_gemv_chain(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s));
     const bool gemv = path == BSR_PATH_GEMV || (path == BSR_PATH_AUTO && small);
     if (gemv) return launched(bsr::launch_gemv(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s));
-    return launched(bsr::launch_gemm(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s));
+    return launched(bsr::launch_gemm(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k,
+                                     path != BSR_PATH_INVARIANT, s));
 }
 
 }  // namespace

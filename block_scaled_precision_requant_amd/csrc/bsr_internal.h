@@ -71,9 +71,11 @@ hipError_t launch_quant_act(const uint16_t *a_bf16, uint8_t *q, float *scale, ui
                             uint32_t group, bool e4m3, hipStream_t s);
 // a_scale row r, block b: a_scale[r * a_ld + (b >> a_shift)] (a_ld = k / 32 and
 // a_shift = 0 for one activation scale per block).
+// split_k: small grids may split K inside a workgroup (a different FP32 sum
+// order per output); false keeps every output one chain over the blocks.
 hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
                        uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
-                       uint32_t k, hipStream_t s);
+                       uint32_t k, bool split_k, hipStream_t s);
 // GEMV whose per-output accumulation follows the GEMM's block order.
 hipError_t launch_gemv_chain(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
                              uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,

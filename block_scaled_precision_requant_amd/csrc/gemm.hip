@@ -165,25 +165,42 @@ __device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "
                  "+v"(x[6]), "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]),    \
                  "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15]))
 
-template <int BM, int BN, int WM, int WN, int WG_PER_CU>
-__global__ __launch_bounds__(BM * BN / (WM * WN) * 64, WG_PER_CU) void gemm_kernel(
+// KG: K groups.  With KG > 1 the workgroup holds KG copies of the wave grid,
+// each with its own ring, walking its own contiguous range of stages; at the
+// end the groups' FP32 tiles are added in group order through LDS.  This
+// splits K inside a workgroup (no memory beyond the output) for grids too
+// small to fill the CUs; the per-output order is then the groups' sum of
+// sequential chains, so the path-invariant mode keeps KG = 1.
+template <int BM, int BN, int WM, int WN, int WG_PER_CU, int KG>
+__global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm_kernel(
     const int8_t *__restrict__ a, const int8_t *__restrict__ w, const float *__restrict__ a_s,
     const float *__restrict__ w_s, uint16_t *__restrict__ out, uint32_t M, uint32_t N, uint32_t K,
     uint32_t a_ld, uint32_t a_shift, uint32_t tiles_m, uint32_t tiles_n) {
     using G = Geo<BM, BN, WM, WN>;
     constexpr int TM = G::kTM, TN = G::kTN;
     using St = Stage<BM, BN>;
-    __shared__ __attribute__((aligned(1024))) St ring[kGemmRing];
+    __shared__ __attribute__((aligned(1024))) St rings[KG][kGemmRing];
+    static_assert(KG == 1 || sizeof(rings) >= sizeof(float) * KG * BM * BN, "the reduction reuses the rings");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave_all / G::kWaves;      // K group
+    const int wave = wave_all % G::kWaves;     // wave within the group's grid
+    St *ring = rings[grp];
     const int wm = wave / G::kWavesN, wn = wave % G::kWavesN;
     uint32_t tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const uint32_t m0 = tm * BM, n0 = tn * BN;
     const uint32_t nb = K / 32;
-    const uint32_t nstages = (nb + kGemmStageBlocks - 1) / kGemmStageBlocks;
+    const uint32_t all_stages = (nb + kGemmStageBlocks - 1) / kGemmStageBlocks;
+    // this group's stages [s_first, s_first + nstages); every group steps
+    // through spg barriers, so groups with fewer stages idle in their tail
+    // (KG == 1: the whole K, with the bounds folded to constants of the loop)
+    const uint32_t spg = KG == 1 ? all_stages : (all_stages + KG - 1) / KG;
+    const uint32_t s_first = KG == 1 ? 0 : min(grp * spg, all_stages);
+    const uint32_t nstages = KG == 1 ? all_stages : min(spg, all_stages - s_first);
+    const uint32_t kend = KG == 1 ? nb : min(nb, (s_first + nstages) * kGemmStageBlocks);  // blocks past it add nothing
 
     // Per-lane LDS offsets of the MFMA operands (constant over the K loop):
     // lane l reads row (l % 32) of its 32-row tile and, for block j, the 16-byte
@@ -219,8 +236,9 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64, WG_PER_CU) void gemm_kern
     auto pair = [&](const St &cur, uint32_t kb, int jp) {
         v4i af[TM][2], bf[TN][2];
         float asv[TM], wsv[TN];
-        // lanes 0-31 carry block jp, lanes 32-63 block jp + 1 (zero if past K)
-        const bool blk_live = kb + jp + half < nb;
+        // lanes 0-31 carry block jp, lanes 32-63 block jp + 1 (zero if past
+        // the group's range)
+        const bool blk_live = kb + jp + half < kend;
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
 #pragma unroll
@@ -271,8 +289,8 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64, WG_PER_CU) void gemm_kern
             for (int j = 0; j < TN; ++j) BSR_PIN16(acc[i][j]);
     };
     auto issue = [&](St &buf, uint32_t stage) {
-        issue_stage<G>(buf, a, w, a_s, w_s, M, N, K, nb, a_ld, a_shift, m0, n0, stage * kGemmStageBlocks, wave,
-                       lane);
+        issue_stage<G>(buf, a, w, a_s, w_s, M, N, K, nb, a_ld, a_shift, m0, n0, (s_first + stage) * kGemmStageBlocks,
+                       wave, lane);
     };
     // Stage s lives in buffer s % 2.  At the top of stage s each wave waits for
     // its own copies of stage s, the barrier publishes every wave's copies and
@@ -282,13 +300,41 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64, WG_PER_CU) void gemm_kern
         wait_copies<0>();
         stage_barrier();
         if (s + 1 < nstages) issue(next, s + 1);
-        compute(cur, s * kGemmStageBlocks);
+        if (KG == 1 || s < nstages) compute(cur, (s_first + s) * kGemmStageBlocks);
     };
-    issue(ring[0], 0);
-    for (uint32_t s = 0; s < nstages; s += 2) {
+    if (KG == 1 || nstages > 0) issue(ring[0], 0);
+    for (uint32_t s = 0; s < spg; s += 2) {
         step(ring[0], ring[1], s);
-        if (s + 1 >= nstages) break;
+        if (s + 1 >= spg) break;
         step(ring[1], ring[0], s + 1);
+    }
+
+    if constexpr (KG > 1) {
+        // Groups' tiles through LDS (the rings are free once every wave has
+        // passed this barrier), summed in group order by group 0.
+        __syncthreads();
+        float *red = reinterpret_cast<float *>(&rings[0][0]);
+        constexpr int kTile = TM * TN * 16;  // floats per lane
+        const uint32_t slot = (uint32_t)(wave * 64 + lane) * kTile;
+        constexpr uint32_t kGroupFloats = G::kWaves * 64 * kTile;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) red[grp * kGroupFloats + slot + (i * TN + j) * 16 + r] = acc[i][j][r];
+        __syncthreads();
+        if (grp != 0) return;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float t = red[slot + (i * TN + j) * 16 + r];
+                    for (int g = 1; g < KG; ++g) t += red[g * kGroupFloats + slot + (i * TN + j) * 16 + r];
+                    acc[i][j][r] = t;
+                }
     }
 
     // Output layout of a 32x32 MFMA tile: lane l holds column l % 32 and, in
@@ -306,14 +352,14 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64, WG_PER_CU) void gemm_kern
         }
 }
 
-template <int BM, int BN, int WM, int WN, int WG_PER_CU>
+template <int BM, int BN, int WM, int WN, int WG_PER_CU, int KG = 1>
 hipError_t launch_tiles(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
                         const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                         uint32_t a_ld, uint32_t a_shift, hipStream_t s) {
     const uint32_t tiles_m = (uint32_t)div_up(m, BM);
     const uint32_t tiles_n = (uint32_t)div_up(n, BN);
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, WG_PER_CU>), dim3(tiles_m * tiles_n),
-                       dim3(Geo<BM, BN, WM, WN>::kThreads), 0, s, a_i8, w_i8, a_scale, w_scale, out, m, n,
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, WG_PER_CU, KG>), dim3(tiles_m * tiles_n),
+                       dim3(Geo<BM, BN, WM, WN>::kThreads * KG), 0, s, a_i8, w_i8, a_scale, w_scale, out, m, n,
                        k, a_ld, a_shift, tiles_m, tiles_n);
     return hipGetLastError();
 }
@@ -322,7 +368,7 @@ hipError_t launch_tiles(const int8_t *a_i8, const int8_t *w_i8, const float *a_s
 
 hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
                        uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
-                       uint32_t k, hipStream_t s) {
+                       uint32_t k, bool split_k, hipStream_t s) {
     // Grids of at least two 128x128 tiles per CU: two 4-wave 128x128
     // workgroups per CU (LDS 2 x 72 KB, 2 x 4 waves of about 230 VGPRs); their
     // barriers fall at different times, so one computes while the other waits
@@ -336,6 +382,14 @@ hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_sc
     if (m > (uint32_t)kGemmBM && big_tiles >= 2 * (uint64_t)kGemmCus)
         return launch_tiles<kGemmBM, kGemmBN, 64, 64, 2>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, a_ld,
                                                          a_shift, s);
+    // At most one 64x64 tile per CU: split K inside the workgroup over 4
+    // groups (one 16-wave workgroup per CU, 144 KB of LDS), when allowed and K
+    // has a stage for every group.
+    const uint64_t small_tiles = div_up(m, kGemmSmallTile) * div_up(n, kGemmSmallTile);
+    const uint32_t stages = (k / 32 + kGemmStageBlocks - 1) / kGemmStageBlocks;
+    if (split_k && small_tiles <= (uint64_t)kGemmCus && stages >= 4)
+        return launch_tiles<kGemmSmallTile, kGemmSmallTile, 32, 32, 1, 4>(a_i8, w_i8, a_scale, w_scale, out, m, n,
+                                                                          k, a_ld, a_shift, s);
     return launch_tiles<kGemmSmallTile, kGemmSmallTile, 32, 32, 2>(a_i8, w_i8, a_scale, w_scale, out, m, n, k,
                                                                    a_ld, a_shift, s);
 }

@@ -1,8 +1,9 @@
 """Path and batch invariance on the GPU: with BSR_PATH_INVARIANT a row's BF16
 bits do not depend on m or on which kernel ran.  For m <= 16 that path runs the
-chain GEMV, which accumulates every output over the K blocks in increasing
-order exactly as the GEMM does, so its output must equal the GEMM path's bit
-for bit -- and both stay within the oracle's tolerance."""
+chain GEMV, for m > 16 the GEMM without its K split, both accumulating every
+output over the K blocks in increasing order, so the same row must give the
+same bits run alone, in a small batch (GEMV) or padded past 16 rows (GEMM) --
+and stay within the oracle's tolerance."""
 import numpy as np
 import pytest
 import torch
@@ -14,6 +15,19 @@ from gpu_util import DEV, gpu_gemm, gpu_gemm_agroup, gpu_quant_act, gpu_requant_
 from oracle.compare import check_bf16
 
 pytestmark = pytest.mark.gpu
+
+PAD = 17  # rows that lift an m <= 16 input onto the GEMM (m > 16)
+
+
+def _padded(t, rows=PAD):
+    """t with `rows` extra rows of its last row appended (same dtype, on the GPU)."""
+    return torch.cat([t, t[-1:].expand(rows, *t.shape[1:])]).contiguous()
+
+
+def _gemm_rows(a_i8, w_i8, a_s, w_s):
+    """The invariant path's GEMM on these rows (padded past 16 rows), first m rows."""
+    m = a_i8.shape[0]
+    return host(gpu_gemm(_padded(a_i8), w_i8, _padded(a_s), w_s, path=bsr.PATH_INVARIANT))[:m]
 
 
 def _operands(seed, m, n, k):
@@ -32,7 +46,7 @@ def test_invariant_gemv_equals_gemm(m, k):
     w_i8, w_s = gpu_requant_w(packed, e4m3, inputs.SCALE2_1_448)
     a_i8, a_s = gpu_requant_a(a)
     inv = host(gpu_gemm(a_i8, w_i8, a_s, w_s, path=bsr.PATH_INVARIANT))
-    ref = host(gpu_gemm(a_i8, w_i8, a_s, w_s, path=bsr.PATH_GEMM))
+    ref = _gemm_rows(a_i8, w_i8, a_s, w_s)
     assert np.array_equal(inv, ref), np.argwhere(inv != ref)[:5]
     oa, osa = oracle.requant_a(a)
     ow, osw = oracle.requant_w(packed, e4m3, inputs.SCALE2_1_448)
@@ -63,7 +77,7 @@ def test_invariant_decode_workloads(name):
     w_i8, w_s = gpu_requant_w(packed, e4m3, p.scale2)
     a_i8, a_s = gpu_requant_a(p.activations())
     inv = host(gpu_gemm(a_i8, w_i8, a_s, w_s, path=bsr.PATH_INVARIANT))
-    ref = host(gpu_gemm(a_i8, w_i8, a_s, w_s, path=bsr.PATH_GEMM))
+    ref = _gemm_rows(a_i8, w_i8, a_s, w_s)
     say(f"{name}: {int((inv != ref).sum())} differing outputs")
     assert np.array_equal(inv, ref)
 
@@ -76,7 +90,8 @@ def test_invariant_grouped_scales(m, group):
     w_i8, w_s = gpu_requant_w(packed, e4m3, inputs.SCALE2_1_448)
     q, s = gpu_quant_act(a, group)
     inv = host(gpu_gemm_agroup(q.view(torch.int8), w_i8, s, group, w_s, path=bsr.PATH_INVARIANT))
-    ref = host(gpu_gemm_agroup(q.view(torch.int8), w_i8, s, group, w_s, path=bsr.PATH_GEMM))
+    ref = host(gpu_gemm_agroup(_padded(q.view(torch.int8)), w_i8, _padded(s), group, w_s,
+                               path=bsr.PATH_INVARIANT))[:m]
     assert np.array_equal(inv, ref)
 
 
@@ -94,10 +109,13 @@ def test_invariant_tiny_scale_products():
     w_s[:, ::7] *= np.float32(2.0 ** 100)
     da, dw, das, dws = to_dev(a_i8), to_dev(w_i8), to_dev(a_s), to_dev(w_s)
     inv = host(gpu_gemm(da, dw, das, dws, path=bsr.PATH_INVARIANT))
-    ref = host(gpu_gemm(da, dw, das, dws, path=bsr.PATH_GEMM))
+    ref = _gemm_rows(da, dw, das, dws)
     y, t = oracle.gemm_ref(a_i8, w_i8, a_s, w_s)
     say(f"tiny scales: {int((inv != ref).sum())} differing outputs; "
         f"gemm {check_bf16(ref, y, t, k)}; chain {check_bf16(inv, y, t, k)}")
+    # the default GEMM path (which may split K) stays within the oracle's rule
+    res = check_bf16(host(gpu_gemm(da, dw, das, dws, path=bsr.PATH_GEMM)), y, t, k)
+    assert res.ok, res
     assert np.array_equal(inv, ref)
 
 
