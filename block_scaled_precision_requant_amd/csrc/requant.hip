@@ -189,12 +189,12 @@ __device__ __forceinline__ float silu_lookup(uint32_t b, const float *tab) {
     const uint32_t key = b & 0x7FFFu;
     const bool neg = b >> 15;
     const uint32_t hi = neg ? neg_hi : pos_hi;
-    const uint32_t idx = min(max(key, lo), hi - 1) - lo + (neg ? kSiluPosBinades * 128 : 0);
-    const float t = tab[idx];
+    // index of the clamped key in its sign's half of the table (one median)
+    const uint32_t base = neg ? kSiluPosBinades * 128 - lo : 0u - lo;
+    const float t = tab[min(max(key, lo), hi - 1) + base];
     const float g = __uint_as_float(b << 16);
-    if (key < lo) return g * 0.5f;
-    if (key >= hi) return neg ? -0.0f : g;
-    return t;
+    const float outer = neg ? -0.0f : g;  // key >= hi
+    return key < lo ? g * 0.5f : (key >= hi ? outer : t);
 }
 
 // binary32 -> the nearest BF16 value (ties to even), kept as a binary32.
