@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsr.so")
 
 BSR_OK, BSR_EINVAL, BSR_ENULL, BSR_EALIGN, BSR_EDEVICE, BSR_ELAUNCH = range(6)
 PATH_AUTO, PATH_GEMM, PATH_GEMV, PATH_INVARIANT = 0, 1, 2, 3
-GEMV_MAX_ROWS = 8
+GEMV_MAX_ROWS = 16
 
 # Exported symbols and their C signatures (kept in step with include/bsr.h).
 _vp, _u32, _f32, _int = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_float, ctypes.c_int
