@@ -24,18 +24,19 @@ constexpr int kSiluThreads = 512;    // lanes per workgroup of the SiLU table ke
 // ---- GEMM (m > 16) --------------------------------------------------------
 // A workgroup computes a BM x BN output tile; each wave owns a WM x WN piece
 // made of 32 x 32 MFMA tiles.  The K loop stages kGemmStageBlocks 32-wide
-// blocks of A, W and their scales per LDS buffer, in a ring of kGemmRing
+// blocks of A, W and their scales per LDS buffer, in a ring of 2 (or 3)
 // buffers.  Workgroups are ordered so that each XCD runs a compact
-// kGemmGroupM-tall group of output tiles.  Two shapes are built: 128 x 128
-// with four 64 x 64 waves, and 64 x 64 with four 32 x 32 waves for grids of
-// the large tile too small to give every CU two workgroups; both run two
-// workgroups per CU.
+// kGemmGroupM-tall group of output tiles.  Shapes: 128 x 128 with four
+// 64 x 64 waves, and 64 x 64 with four 32 x 32 waves for grids of the large
+// tile too small to give every CU two workgroups; both run two workgroups per
+// CU.  Grids with at most one or two tiles per CU split K inside the
+// workgroup over groups of waves (64 x 64 or 32 x 32 tiles).
 constexpr int kGemmBM = 128;
 constexpr int kGemmBN = 128;
 constexpr int kGemmSmallTile = 64;
+constexpr int kGemmTinyTile = 32;
 constexpr int kGemmStageBlocks = 4;
 constexpr int kGemmStageBytes = 32 * kGemmStageBlocks;    // 128 bytes of K per row: whole cache lines
-constexpr int kGemmRing = 2;                              // stage buffers in flight
 constexpr int kGemmGroupM = 8;
 constexpr int kXcds = 8;
 constexpr int kGemmCus = 256;                             // compute units of an MI355X

@@ -15,8 +15,9 @@
 // Operand staging: a stage is kGemmStageBlocks blocks (128 bytes of every A
 // and W row, i.e. whole cache lines) plus the matching scales, copied straight
 // from global memory into LDS with global_load_lds (no registers held while
-// the copy is in flight) into a ring of kGemmRing buffers; the next stage is
-// in flight while the current one is computed, with one barrier per stage.
+// the copy is in flight) into a ring of RING buffers; the next RING - 1
+// stages are in flight while the current one is computed, with one barrier
+// per stage.
 #include "bsr_internal.h"
 
 namespace bsr {
@@ -31,7 +32,6 @@ constexpr int kChunksPerRow = kGemmStageBytes / 16;   // 8
 constexpr int kRowsPerCopy = 64 / kChunksPerRow;      // 8 rows per 1 KB wave copy
 static_assert(kChunksPerRow == 8, "the chunk swizzle permutes 8 chunks per row");
 static_assert(kGemmStageBlocks % 2 == 0, "the 2-block f32 MFMA covers pairs of blocks");
-static_assert(kGemmRing == 2, "the loop below alternates two buffers");
 
 // Geometry of one tile shape.
 template <int BM, int BN, int WM, int WN>
@@ -139,6 +139,20 @@ __device__ __forceinline__ void issue_stage(Stage<BM, BN> &st, const int8_t *a, 
     copy_scales<BN * kGemmStageBlocks / 64, G::kWaves>(&st.ws[0][0], w_s, N, n0, nb, 0, nb, kb, wave, lane);
 }
 
+// Copies one wave issues per stage, when every operand's segments divide
+// evenly among the waves (required for rings deeper than 2, whose waits count
+// the copies of later stages).
+template <class G, int BM, int BN>
+constexpr int stage_copies() {
+    return (BM / kRowsPerCopy + BN / kRowsPerCopy + BM * kGemmStageBlocks / 64 + BN * kGemmStageBlocks / 64) /
+           G::kWaves;
+}
+template <class G, int BM, int BN>
+constexpr bool even_copies() {
+    return (BM / kRowsPerCopy) % G::kWaves == 0 && (BN / kRowsPerCopy) % G::kWaves == 0 &&
+           (BM * kGemmStageBlocks / 64) % G::kWaves == 0 && (BN * kGemmStageBlocks / 64) % G::kWaves == 0;
+}
+
 // Wait until at most n of this wave's global -> LDS copies are outstanding.
 // Copies complete in issue order, so this waits for every older stage.
 // (s_waitcnt on gfx9: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt
@@ -147,6 +161,22 @@ template <int n>
 __device__ __forceinline__ void wait_copies() {
     static_assert(n >= 0 && n < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+}
+
+// Wait for a stage's copies while the copies of the `later` stages issued
+// after it (C per stage, later <= N) stay in flight: s_waitcnt takes an
+// immediate, so one branch per count.
+template <int C, int N>
+__device__ __forceinline__ void wait_later_stages(uint32_t later) {
+    if constexpr (N > 0) {
+        if (later == (uint32_t)N) {
+            wait_copies<C * N>();
+            return;
+        }
+        wait_later_stages<C, N - 1>(later);
+    } else {
+        wait_copies<0>();
+    }
 }
 
 // Workgroup barrier without the release/acquire fences of __syncthreads():
@@ -171,7 +201,7 @@ __device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "
 // splits K inside a workgroup (no memory beyond the output) for grids too
 // small to fill the CUs; the per-output order is then the groups' sum of
 // sequential chains, so the path-invariant mode keeps KG = 1.
-template <int BM, int BN, int WM, int WN, int WG_PER_CU, int KG>
+template <int BM, int BN, int WM, int WN, int WG_PER_CU, int KG, int RING>
 __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm_kernel(
     const int8_t *__restrict__ a, const int8_t *__restrict__ w, const float *__restrict__ a_s,
     const float *__restrict__ w_s, uint16_t *__restrict__ out, uint32_t M, uint32_t N, uint32_t K,
@@ -179,7 +209,11 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
     using G = Geo<BM, BN, WM, WN>;
     constexpr int TM = G::kTM, TN = G::kTN;
     using St = Stage<BM, BN>;
-    __shared__ __attribute__((aligned(1024))) St rings[KG][kGemmRing];
+    __shared__ __attribute__((aligned(1024))) St rings[KG][RING];
+    static_assert(RING >= 2, "a ring of at least two buffers");
+    static_assert(RING == 2 || even_copies<G, BM, BN>(), "deeper rings count uniform copies per wave");
+    constexpr int kCopies = stage_copies<G, BM, BN>();
+    static_assert(kCopies * (RING - 2) < 64, "the copies in flight fit the vmcnt range");
     static_assert(KG == 1 || sizeof(rings) >= sizeof(float) * KG * BM * BN, "the reduction reuses the rings");
 
     const int tid = threadIdx.x;
@@ -292,21 +326,26 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
         issue_stage<G>(buf, a, w, a_s, w_s, M, N, K, nb, a_ld, a_shift, m0, n0, (s_first + stage) * kGemmStageBlocks,
                        wave, lane);
     };
-    // Stage s lives in buffer s % 2.  At the top of stage s each wave waits for
-    // its own copies of stage s, the barrier publishes every wave's copies and
-    // frees the other buffer (its stage s - 1 reads are done), and the copies of
-    // stage s + 1 go out before stage s is computed.
-    auto step = [&](St &cur, St &next, uint32_t s) {
-        wait_copies<0>();
+    // Stage s lives in buffer s % RING.  At the top of stage s each wave waits
+    // for its own copies of stage s (those of the up to RING - 2 later stages
+    // already issued may stay in flight), the barrier publishes every wave's
+    // copies and frees buffer (s - 1) % RING (its reads are done), and the
+    // copies of stage s + RING - 1 go into it before stage s is computed.
+    auto step = [&](int u, uint32_t s) {
+        wait_later_stages<kCopies, RING - 2>(s < nstages ? min(nstages - 1 - s, (uint32_t)RING - 2) : 0);
         stage_barrier();
-        if (s + 1 < nstages) issue(next, s + 1);
-        if (KG == 1 || s < nstages) compute(cur, (s_first + s) * kGemmStageBlocks);
+        if (s + RING - 1 < nstages) issue(ring[(u + RING - 1) % RING], s + RING - 1);
+        if (KG == 1 || s < nstages) compute(ring[u], (s_first + s) * kGemmStageBlocks);
     };
-    if (KG == 1 || nstages > 0) issue(ring[0], 0);
-    for (uint32_t s = 0; s < spg; s += 2) {
-        step(ring[0], ring[1], s);
-        if (s + 1 >= spg) break;
-        step(ring[1], ring[0], s + 1);
+#pragma unroll
+    for (int r = 0; r < RING - 1; ++r)
+        if ((KG == 1 && r == 0) || (uint32_t)r < nstages) issue(ring[r], r);  // (KG == 1: K has a stage)
+    for (uint32_t s = 0; s < spg; s += RING) {
+#pragma unroll
+        for (int u = 0; u < RING; ++u) {
+            if (u > 0 && s + u >= spg) break;
+            step(u, s + u);
+        }
     }
 
     if constexpr (KG > 1) {
@@ -352,13 +391,13 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
         }
 }
 
-template <int BM, int BN, int WM, int WN, int WG_PER_CU, int KG = 1>
+template <int BM, int BN, int WM, int WN, int WG_PER_CU, int KG = 1, int RING = 2>
 hipError_t launch_tiles(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
                         const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                         uint32_t a_ld, uint32_t a_shift, hipStream_t s) {
     const uint32_t tiles_m = (uint32_t)div_up(m, BM);
     const uint32_t tiles_n = (uint32_t)div_up(n, BN);
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, WG_PER_CU, KG>), dim3(tiles_m * tiles_n),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, WG_PER_CU, KG, RING>), dim3(tiles_m * tiles_n),
                        dim3(Geo<BM, BN, WM, WN>::kThreads * KG), 0, s, a_i8, w_i8, a_scale, w_scale, out, m, n,
                        k, a_ld, a_shift, tiles_m, tiles_n);
     return hipGetLastError();
@@ -382,14 +421,27 @@ hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_sc
     if (m > (uint32_t)kGemmBM && big_tiles >= 2 * (uint64_t)kGemmCus)
         return launch_tiles<kGemmBM, kGemmBN, 64, 64, 2>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, a_ld,
                                                          a_shift, s);
-    // At most one 64x64 tile per CU: split K inside the workgroup over 4
-    // groups (one 16-wave workgroup per CU, 144 KB of LDS), when allowed and K
-    // has a stage for every group.
+    // Small grids, when K may be split inside a workgroup (its K groups each
+    // walk a contiguous range of stages; the FP32 tiles are summed in group
+    // order at the end) and K has a stage for every group:
+    //  * at most one 32x32 tile per CU: 8 one-wave groups per workgroup
+    //    (144 KB of LDS), e.g. m <= 64 at n = 4096, 2x faster than 64x64 tiles;
+    //  * at most two: 4 groups, two workgroups per CU (72 KB each) -- also
+    //    pads m = 17-32 to 32 rows instead of 64;
+    //  * at most one 64x64 tile per CU: 2 groups of four 32x32 waves, each
+    //    with a 3-deep ring (two stages in flight while one is computed).
+    const uint64_t t32 = div_up(m, kGemmTinyTile) * div_up(n, kGemmTinyTile);
     const uint64_t small_tiles = div_up(m, kGemmSmallTile) * div_up(n, kGemmSmallTile);
     const uint32_t stages = (k / 32 + kGemmStageBlocks - 1) / kGemmStageBlocks;
-    if (split_k && small_tiles <= (uint64_t)kGemmCus && stages >= 4)
-        return launch_tiles<kGemmSmallTile, kGemmSmallTile, 32, 32, 1, 4>(a_i8, w_i8, a_scale, w_scale, out, m, n,
-                                                                          k, a_ld, a_shift, s);
+    if (split_k && t32 <= (uint64_t)kGemmCus && stages >= 8)
+        return launch_tiles<kGemmTinyTile, kGemmTinyTile, 32, 32, 1, 8>(a_i8, w_i8, a_scale, w_scale, out, m, n, k,
+                                                                         a_ld, a_shift, s);
+    if (split_k && t32 <= 2 * (uint64_t)kGemmCus && stages >= 4)
+        return launch_tiles<kGemmTinyTile, kGemmTinyTile, 32, 32, 2, 4>(a_i8, w_i8, a_scale, w_scale, out, m, n, k,
+                                                                         a_ld, a_shift, s);
+    if (split_k && small_tiles <= (uint64_t)kGemmCus && stages >= 2)
+        return launch_tiles<kGemmSmallTile, kGemmSmallTile, 32, 32, 1, 2, 3>(a_i8, w_i8, a_scale, w_scale, out, m,
+                                                                             n, k, a_ld, a_shift, s);
     return launch_tiles<kGemmSmallTile, kGemmSmallTile, 32, 32, 2>(a_i8, w_i8, a_scale, w_scale, out, m, n, k,
                                                                    a_ld, a_shift, s);
 }

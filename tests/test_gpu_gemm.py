@@ -35,12 +35,16 @@ def _check(name, out_bits, y, t, k):
     return res
 
 
-# Small grids split K over 4 or 2 groups inside a workgroup: uneven group
-# ranges (544: 5 stages; 4128: 33 stages with a partial last one), an empty
-# group, and K too short to split (96, 32) are all here.
+# Small grids split K over 8, 4 or 2 groups inside a workgroup (32x32 tiles
+# for at most one or two tiles per CU, else 64x64): uneven group ranges (544:
+# 5 stages; 4128: 33 stages with a partial last one), empty groups, and K too
+# short to split (96, 32) are all here; (20, 14336, 4096) and (100, 3000,
+# 2048) take the 4-group 32x32 tiles, (128, 4200, 1024) and (37, 1000, 160)
+# the 2-group 64x64 tiles, (64, 4096, 4096) the 8-group 32x32 tiles.
 @pytest.mark.parametrize("m,n,k", [(16, 256, 512), (200, 300, 544), (129, 257, 96), (9, 33, 32),
                                    (1000, 130, 1024), (256, 128, 4096), (37, 1000, 160),
-                                   (48, 1000, 14336), (17, 512, 4128), (100, 200, 1056), (300, 700, 2080)])
+                                   (48, 1000, 14336), (17, 512, 4128), (100, 200, 1056), (300, 700, 2080),
+                                   (20, 14336, 4096), (100, 3000, 2048), (128, 4200, 1024), (64, 4096, 4096)])
 def test_gemm_parity_random(m, n, k):
     say(f"gemm random m={m} n={n} k={k}")
     a, w, a_s, w_s = _rand_operands(m * 7 + n * 13 + k, m, n, k, zero_frac=0.05)
