@@ -43,10 +43,11 @@ constexpr int kGemmCus = 256;                             // compute units of an
 
 // ---- GEMV (m <= 16) -------------------------------------------------------
 // A workgroup owns kGemvCols output columns and splits K over its waves; each
-// wave runs v_mfma_i32_16x16x64_i8 on (activation rows padded to 16) x (16
-// weight rows), one 64-byte K step at a time, the two 32-wide blocks of a step
-// separated by zeroing half of the activation operand.  The waves' FP32
-// partial sums are added in LDS in a fixed order.
+// wave runs 16-row MFMA tiles on (activation rows padded to 16) x (16 weight
+// rows): v_mfma_i32_16x16x32_i8 per 32-wide block in the streamed kernel (K a
+// multiple of 256), else v_mfma_i32_16x16x64_i8 per 64-byte step with the two
+// blocks separated by zeroing half of the activation operand.  The waves'
+// FP32 partial sums are added in LDS in a fixed order.
 constexpr int kGemvCols = 16;
 constexpr int kGemvMaxWaves = 16;
 constexpr int kGemvMaxRows = 16;  // the rows of one 16x16 MFMA output tile

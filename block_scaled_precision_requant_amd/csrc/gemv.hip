@@ -19,6 +19,11 @@
 // the 16 rows of the MFMA cover m <= 16 at no extra matrix-core cost.
 //
 // Kernels:
+//  * stream (K a multiple of 256): each wave brings its K range through a
+//    private LDS ring with global_load_lds, 1 KB copies of whole cache lines
+//    -- weight rows, activation rows and scales alike -- and takes one
+//    v_mfma_i32_16x16x32_i8 per block; about three times the per-CU copy
+//    rate of loading 16 rows x 64 bytes per instruction into registers;
 //  * staged: the workgroup first copies its activations, activation scales
 //    and the scales of its 16 weight rows into LDS (global_load_lds), so the
 //    only global loads of the K loop are weight bytes -- one 1 KB instruction
@@ -103,6 +108,21 @@ template <int n>
 __device__ __forceinline__ void wait_vm_le() {
     static_assert(n >= 0 && n < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+}
+
+// Wait until at most C * later copies are outstanding (later <= N): s_waitcnt
+// takes an immediate, so one branch per count.
+template <int C, int N>
+__device__ __forceinline__ void wait_vm_later(uint32_t later) {
+    if constexpr (N > 0) {
+        if (later == (uint32_t)N) {
+            wait_vm_le<C * N>();
+            return;
+        }
+        wait_vm_later<C, N - 1>(later);
+    } else {
+        wait_vm_le<0>();
+    }
 }
 
 // ---------------------------------------------------------------- direct
@@ -570,6 +590,165 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void gemv_staged_kernel(
     gemv_reduce_store(reinterpret_cast<float *>(smem), acc, wave, nwaves, lane, n0, m, n, out);
 }
 
+// ---------------------------------------------------------------- stream
+
+// Streamed GEMV (K a multiple of 256): the waves
+// split K into contiguous ranges of 8-block chunks, and each wave brings its
+// chunks -- 16 weight rows, the activation rows and both scale tiles --
+// through a private LDS ring with global_load_lds, 1 KB per copy (4 rows of
+// 256 bytes, whole cache lines), RING - 1 chunks in flight while one is
+// computed.  The arithmetic per 4 blocks is the chain kernel's: four
+// v_mfma_i32_16x16x32_i8 and one v_mfma_f32_16x16x1f32 of scale products.
+// The waves' partial sums are added in wave order at the end.  AGROUP:
+// activation scales per 2^a_shift blocks, expanded to one per block by 4-byte
+// copies.
+constexpr int kStreamChunkBlocks = 8;
+constexpr int kStreamRowBytes = kStreamChunkBlocks * 32;  // 256: 16 slots of 16 bytes
+constexpr int kStreamRowsPerCopy = 1024 / kStreamRowBytes;
+// LDS rows are unpadded; 16-byte slot c of row r holds chunk c ^ (r & 15), so
+// the 16 rows a quarter-wave reads at one offset fall in 16 distinct slots.
+template <int ROWS>
+struct StreamBuf {
+    static constexpr int kARows = ROWS < kStreamRowsPerCopy ? kStreamRowsPerCopy : ROWS;
+    int8_t w[kGemvCols * kStreamRowBytes];
+    int8_t a[kARows * kStreamRowBytes];
+    float s[32][kStreamChunkBlocks];  // w_s rows 0-15, a_s rows 16..16+ROWS-1
+};
+template <int ROWS, bool AGROUP>
+constexpr int stream_copies() {  // copies per chunk, each with live lanes
+    return kGemvCols / kStreamRowsPerCopy + StreamBuf<ROWS>::kARows / kStreamRowsPerCopy + 1 +
+           (AGROUP ? (ROWS * kStreamChunkBlocks + 63) / 64 : 0);
+}
+
+template <int ROWS, int RING, bool AGROUP>
+__global__ __launch_bounds__(kGemvMaxWaves * 64) void gemv_stream_kernel(
+    const int8_t *__restrict__ a, const int8_t *w, const float *__restrict__ a_s,
+    const float *__restrict__ w_s, uint16_t *__restrict__ out, uint32_t m, uint32_t n, uint32_t k,
+    uint32_t a_ld, uint32_t a_shift, uint32_t cpw) {
+    using Buf = StreamBuf<ROWS>;
+    constexpr int NC = stream_copies<ROWS, AGROUP>();
+    static_assert(NC * (RING - 1) < 64, "the copies in flight fit the vmcnt range");
+    static_assert(ROWS <= 16, "one 16-row MFMA tile");
+    extern __shared__ __attribute__((aligned(1024))) int8_t smem[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nwaves = blockDim.x >> 6;
+    const int q = lane >> 4;
+    const uint32_t c16 = lane & 15;
+    const uint32_t n0 = blockIdx.x * kGemvCols;
+    const uint32_t nb = k / 32;  // a multiple of 8
+    const uint32_t c_begin = wave * cpw;
+    const uint32_t nchunks = min(nb / kStreamChunkBlocks, c_begin + cpw) - c_begin;  // >= 1
+    Buf *ring = reinterpret_cast<Buf *>(smem) + wave * RING;
+
+    // Copy lane roles: byte copies take row (lane / 16) of a 4-row group and
+    // LDS slot lane % 16, fetching chunk slot ^ row; the 16-byte scale copy
+    // takes row lane / 2 (weight rows, then per-block activation rows) and
+    // half lane % 2; a 4-byte grouped-scale copy takes activation row
+    // 8 i + lane / 8 and block lane % 8.
+    const uint32_t slot = lane & 15;
+    const uint32_t srow = lane >> 1;
+    const bool s_live = srow < (uint32_t)(AGROUP ? kGemvCols : kGemvCols + ROWS);
+    const float *s_src = srow < (uint32_t)kGemvCols
+                             ? w_s + (uint64_t)min(n0 + srow, n - 1) * nb
+                             : a_s + (uint64_t)min(srow - kGemvCols, m - 1) * a_ld;
+    auto issue = [&](int bi, uint32_t chunk) {
+        Buf &b = ring[bi];
+        const uint32_t kb = (c_begin + chunk) * kStreamChunkBlocks;
+#pragma unroll
+        for (int i = 0; i < kGemvCols / kStreamRowsPerCopy; ++i) {
+            const uint32_t r = i * kStreamRowsPerCopy + (lane >> 4);
+            const int8_t *src = w + (uint64_t)min(n0 + r, n - 1) * k + kb * 32 + ((slot ^ (r & 15)) << 4);
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(b.w + i * 1024), 16, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < Buf::kARows / kStreamRowsPerCopy; ++i) {
+            const uint32_t r = i * kStreamRowsPerCopy + (lane >> 4);
+            const int8_t *src = a + (uint64_t)min(r, m - 1) * k + kb * 32 + ((slot ^ (r & 15)) << 4);
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(b.a + i * 1024), 16, 0, 0);
+        }
+        if (s_live)
+            __builtin_amdgcn_global_load_lds(s_src + kb + 4 * (lane & 1), (lds_void *)(&b.s[0][0]), 16, 0, 0);
+        if constexpr (AGROUP) {
+#pragma unroll
+            for (int i = 0; i < (ROWS * kStreamChunkBlocks + 63) / 64; ++i) {
+                const uint32_t r = 8 * i + (lane >> 3);
+                if (r < (uint32_t)ROWS)
+                    __builtin_amdgcn_global_load_lds(a_s + (uint64_t)min(r, m - 1) * a_ld + ((kb + (lane & 7)) >> a_shift),
+                                                     (lds_void *)(&b.s[kGemvCols + 8 * i][0]), 4, 0, 0);
+            }
+        }
+    };
+
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t arow = min(c16, (uint32_t)ROWS - 1);
+    auto compute = [&](int bi) {
+        const Buf &b = ring[bi];
+        const int8_t *wr = b.w + c16 * kStreamRowBytes;
+        const int8_t *ar = b.a + arow * kStreamRowBytes;
+        auto off = [&](uint32_t r, int blk) {  // byte offset of this lane's 8 bytes of a block
+            return ((((uint32_t)(2 * blk) + (q >> 1)) ^ (r & 15)) << 4) + 8 * (q & 1);
+        };
+        const v4i zero4 = {0, 0, 0, 0};
+        const v16f zero16 = {};
+        ChainOps x[2];
+        auto read = [&](ChainOps &o, int i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                o.av[j] = *reinterpret_cast<const long *>(ar + off(arow, 4 * i + j));
+                o.wv[j] = *reinterpret_cast<const long *>(wr + off(c16, 4 * i + j));
+            }
+            o.as = b.s[kGemvCols + arow][4 * i + q];
+            o.ws = b.s[c16][4 * i + q];
+        };
+        read(x[0], 0);
+#pragma unroll
+        for (int i = 0; i < kStreamChunkBlocks / 4; ++i) {
+            if (i + 1 < kStreamChunkBlocks / 4) read(x[(i + 1) & 1], i + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const ChainOps &cur = x[i & 1];
+            v4i p[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(cur.av[j], cur.wv[j], zero4, 0, 0, 0);
+            const v16f sc = __builtin_amdgcn_mfma_f32_16x16x1f32(cur.as, cur.ws, zero16, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = fmaf((float)p[j][r], sc[4 * j + r], acc[r]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto reads_done = [&]() {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+    };
+    // Before computing chunk c (after issuing chunk c + RING - 1): its copies
+    // are done; those of the up to RING - 1 later chunks may stay in flight.
+    auto wait_chunk = [&](uint32_t c) {
+        wait_vm_later<NC, RING - 1>(min(nchunks - 1 - c, (uint32_t)RING - 1));
+        asm volatile("" ::: "memory");
+    };
+
+#pragma unroll
+    for (int r = 0; r < RING - 1; ++r)
+        if ((uint32_t)r < nchunks) issue(r, r);
+    for (uint32_t c0 = 0; c0 < nchunks; c0 += RING) {
+#pragma unroll
+        for (int u = 0; u < RING; ++u) {
+            const uint32_t c = c0 + u;
+            if (c >= nchunks) break;
+            // buffer (u + RING - 1) % RING held chunk c - 1, whose reads are done
+            if (c + RING - 1 < nchunks) issue((u + RING - 1) % RING, c + RING - 1);
+            wait_chunk(c);
+            compute(u);
+            reads_done();
+        }
+    }
+    __syncthreads();  // every wave is done with its ring
+    gemv_reduce_store(reinterpret_cast<float *>(smem), acc, wave, nwaves, lane, n0, m, n, out);
+}
+
 }  // namespace
 
 hipError_t launch_gemv_chain(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
@@ -617,9 +796,52 @@ hipError_t launch_gemv_chain(const int8_t *a_i8, const int8_t *w_i8, const float
     return hipGetLastError();
 }
 
+namespace {
+
+// Streamed GEMV launch (k a multiple of 256).  Waves per workgroup: about
+// 2048 waves over the grid, 2 to 8 per workgroup (4 for grids of 1024
+// workgroups or more); each wave gets an equal run of chunks.  The ring is
+// double-buffered: deeper rings measured no faster once the grid holds ~8
+// waves per CU.
+template <int ROWS, bool AGROUP>
+hipError_t launch_stream(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
+                         uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
+                         uint32_t k, hipStream_t s) {
+    constexpr int kRing = 2;
+    const uint32_t tiles = (uint32_t)div_up(n, kGemvCols);
+    const uint32_t nchunks = k / 32 / kStreamChunkBlocks;
+    uint32_t waves = tiles >= 1024 ? 4u : max(2u, min(8u, 2048u / tiles));
+    waves = min(waves, nchunks);
+    const uint32_t cpw = (uint32_t)div_up(nchunks, waves);
+    waves = (uint32_t)div_up(nchunks, cpw);
+    const uint32_t lds = max(waves * kRing * (uint32_t)sizeof(StreamBuf<ROWS>), kRedBytes);
+    static_assert(8 * kRing * sizeof(StreamBuf<16>) <= kLdsBytes, "eight waves' rings fit in LDS");
+    hipLaunchKernelGGL((gemv_stream_kernel<ROWS, kRing, AGROUP>), dim3(tiles), dim3(64 * waves), lds, s, a_i8, w_i8,
+                       a_scale, w_scale, out, m, n, k, a_ld, a_shift, cpw);
+    return hipGetLastError();
+}
+
+template <bool AGROUP>
+hipError_t launch_stream_rows(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
+                              uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
+                              uint32_t k, hipStream_t s) {
+    if (m <= 1) return launch_stream<1, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+    if (m <= 2) return launch_stream<2, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+    if (m <= 4) return launch_stream<4, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+    if (m <= 8) return launch_stream<8, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+    return launch_stream<16, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+}
+
+}  // namespace
+
 hipError_t launch_gemv(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
                        uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
                        uint32_t k, hipStream_t s) {
+    if (k % (32 * kStreamChunkBlocks) == 0) {
+        if (a_shift) return launch_stream_rows<true>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+        return launch_stream_rows<false>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+    }
+    // Other K: the staged kernel when its slices fit in LDS, else the direct one.
     // Waves per workgroup: enough that the whole launch has ~24 waves per CU
     // (6144 waves over 256 CUs), but at least one iteration per wave.  The
     // staged kernel also needs at most kStagedMaxIters iterations per wave.
