@@ -15,7 +15,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsr.so")
 
 BSR_OK, BSR_EINVAL, BSR_ENULL, BSR_EALIGN, BSR_EDEVICE, BSR_ELAUNCH = range(6)
 PATH_AUTO, PATH_GEMM, PATH_GEMV, PATH_INVARIANT = 0, 1, 2, 3
-GEMV_MAX_ROWS = 16
+GEMV_MAX_ROWS = 16          # any K
+GEMV_STREAM_MAX_ROWS = 64   # K a multiple of 256
 
 # Exported symbols and their C signatures (kept in step with include/bsr.h).
 _vp, _u32, _f32, _int = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_float, ctypes.c_int
@@ -158,7 +159,8 @@ def int8_gemm_blockscaled_ex(a_i8, w_i8, a_scale, w_scale, out, path=PATH_AUTO, 
 
 
 def int8_gemm_blockscaled(a_i8, w_i8, a_scale, w_scale, out, stream=None):
-    """As int8_gemm_blockscaled_ex with the automatic path (GEMV iff M <= 16)."""
+    """As int8_gemm_blockscaled_ex with the automatic path (the GEMV for M <= 16, and for
+    M <= 48 when K % 256 == 0 and N <= 4096; else the GEMM)."""
     m, k = a_i8.shape
     n = w_i8.shape[0]
     _shape(a_i8, (m, k), "a_i8")

@@ -1,4 +1,4 @@
-// api.hip -- the C ABI of libbsr: argument validation, the m <= 16 dispatch
+// api.hip -- the C ABI of libbsr: argument validation, the GEMV/GEMM dispatch
 // and the launches.  Every check happens before the first launch; an error
 // launches nothing.  The only state is a per-device cache of the gfx950 check.
 #include <atomic>
@@ -31,6 +31,13 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 bool k_ok(uint32_t k) { return k != 0 && k % 32 == 0; }
 
+// Rows the GEMV takes: one 16-row tile at any K, up to four when K suits the
+// streamed kernel.
+bool gemv_rows_ok(uint32_t m, uint32_t k) {
+    return m <= (uint32_t)bsr::kGemvMaxRows ||
+           (m <= (uint32_t)bsr::kGemvStreamMaxRows && k % bsr::kGemvStreamKAlign == 0);
+}
+
 // Grids stay below 2^31 workgroups.
 constexpr uint64_t kMaxGrid = (1ull << 31) - 1;
 
@@ -43,7 +50,7 @@ int gemm_args_check(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale
     if (path != BSR_PATH_AUTO && path != BSR_PATH_GEMM && path != BSR_PATH_GEMV && path != BSR_PATH_INVARIANT)
         return BSR_EINVAL;
     if (m == 0 || n == 0) return BSR_OK;
-    if (path == BSR_PATH_GEMV && m > (uint32_t)bsr::kGemvMaxRows) return BSR_EINVAL;
+    if (path == BSR_PATH_GEMV && !gemv_rows_ok(m, k)) return BSR_EINVAL;
     if (!a_i8 || !w_i8 || !a_scale || !w_scale || !out) return BSR_ENULL;
     if (!aligned(a_i8, 16) || !aligned(w_i8, 16) || !aligned(a_scale, 4) || !aligned(w_scale, 4) ||
         !aligned(out, 2))
@@ -118,7 +125,12 @@ int gemm_launch(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, ui
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (path == BSR_PATH_INVARIANT && small)
         return launched(bsr::launch_gemv_chain(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s));
-    const bool gemv = path == BSR_PATH_GEMV || (path == BSR_PATH_AUTO && small);
+    // The automatic path also takes the streamed GEMV for a few tiles of rows
+    // when the grid is narrow (measured faster than the GEMM's small-grid
+    // tiles up to 48 rows at n <= 4096; slower at n = 14336).
+    const bool narrow = bsr::div_up(n, bsr::kGemvCols) <= (uint64_t)bsr::kGemmCus;
+    const bool stream_rows = m <= (uint32_t)bsr::kGemvStreamAutoRows && k % bsr::kGemvStreamKAlign == 0 && narrow;
+    const bool gemv = path == BSR_PATH_GEMV || (path == BSR_PATH_AUTO && (small || stream_rows));
     if (gemv) return launched(bsr::launch_gemv(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s));
     return launched(bsr::launch_gemm(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k,
                                      path != BSR_PATH_INVARIANT, s));

@@ -51,6 +51,12 @@ constexpr int kGemmCus = 256;                             // compute units of an
 constexpr int kGemvCols = 16;
 constexpr int kGemvMaxWaves = 16;
 constexpr int kGemvMaxRows = 16;  // the rows of one 16x16 MFMA output tile
+// The streamed GEMV (K a multiple of kGemvStreamKAlign) takes up to four
+// 16-row tiles; the automatic path uses it for m <= kGemvStreamAutoRows when
+// the grid has at most one 16-column workgroup per CU.
+constexpr int kGemvStreamMaxRows = 64;
+constexpr int kGemvStreamAutoRows = 48;
+constexpr int kGemvStreamKAlign = 256;
 constexpr int kGemvBlocksPerIter = 4;   // K blocks per loop iteration of a wave (two MFMA steps)
 
 // ---- W4A16 decode GEMV (m <= 16, straight from NVFP4) -----------------------
@@ -82,6 +88,7 @@ hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_sc
 hipError_t launch_gemv_chain(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
                              uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
                              uint32_t k, hipStream_t s);
+// m <= kGemvMaxRows, or m <= kGemvStreamMaxRows with k % kGemvStreamKAlign == 0.
 hipError_t launch_gemv(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
                        uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
                        uint32_t k, hipStream_t s);

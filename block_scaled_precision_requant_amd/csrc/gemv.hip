@@ -592,17 +592,17 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void gemv_staged_kernel(
 
 // ---------------------------------------------------------------- stream
 
-// Streamed GEMV (K a multiple of 256): the waves
-// split K into contiguous ranges of 8-block chunks, and each wave brings its
-// chunks -- 16 weight rows, the activation rows and both scale tiles --
-// through a private LDS ring with global_load_lds, 1 KB per copy (4 rows of
-// 256 bytes, whole cache lines), RING - 1 chunks in flight while one is
-// computed.  The arithmetic per 4 blocks is the chain kernel's: four
-// v_mfma_i32_16x16x32_i8 and one v_mfma_f32_16x16x1f32 of scale products.
-// The waves' partial sums are added in wave order at the end.  AGROUP:
-// activation scales per 2^a_shift blocks, expanded to one per block by 4-byte
-// copies.
-constexpr int kStreamChunkBlocks = 8;
+// Streamed GEMV (K a multiple of 256): the waves split K into contiguous
+// ranges of 8-block chunks, and each wave brings its chunks -- 16 weight
+// rows, the activation rows and both scale tiles -- through a private LDS
+// ring with global_load_lds, 1 KB per copy (4 rows of 256 bytes, whole cache
+// lines), RING - 1 chunks in flight while one is computed.  Per 4 blocks and
+// 16-row activation tile: four v_mfma_i32_16x16x32_i8 and one
+// v_mfma_f32_16x16x1f32 of scale products, as in the chain kernel; up to four
+// tiles (m <= 64) share each weight chunk.  The waves' partial sums are added
+// in wave order at the end.  AGROUP: activation scales per 2^a_shift blocks,
+// expanded to one per block by 4-byte copies.
+constexpr int kStreamChunkBlocks = kGemvStreamKAlign / 32;
 constexpr int kStreamRowBytes = kStreamChunkBlocks * 32;  // 256: 16 slots of 16 bytes
 constexpr int kStreamRowsPerCopy = 1024 / kStreamRowBytes;
 // LDS rows are unpadded; 16-byte slot c of row r holds chunk c ^ (r & 15), so
@@ -610,25 +610,34 @@ constexpr int kStreamRowsPerCopy = 1024 / kStreamRowBytes;
 template <int ROWS>
 struct StreamBuf {
     static constexpr int kARows = ROWS < kStreamRowsPerCopy ? kStreamRowsPerCopy : ROWS;
+    static constexpr int kSRows = kGemvCols + ROWS;  // w_s rows, then a_s rows
     int8_t w[kGemvCols * kStreamRowBytes];
     int8_t a[kARows * kStreamRowBytes];
-    float s[32][kStreamChunkBlocks];  // w_s rows 0-15, a_s rows 16..16+ROWS-1
+    float s[kSRows][kStreamChunkBlocks];
 };
 template <int ROWS, bool AGROUP>
-constexpr int stream_copies() {  // copies per chunk, each with live lanes
-    return kGemvCols / kStreamRowsPerCopy + StreamBuf<ROWS>::kARows / kStreamRowsPerCopy + 1 +
-           (AGROUP ? (ROWS * kStreamChunkBlocks + 63) / 64 : 0);
-}
+struct StreamCopies {  // copy instructions per chunk, each with live lanes
+    static constexpr int kScale16 = AGROUP ? 1 : (kGemvCols + ROWS + 31) / 32;  // 32 rows per copy
+    static constexpr int kScale4 = AGROUP ? (ROWS + 7) / 8 : 0;                  // 8 rows per copy
+    static constexpr int kTotal =
+        kGemvCols / kStreamRowsPerCopy + StreamBuf<ROWS>::kARows / kStreamRowsPerCopy + kScale16 + kScale4;
+};
+
+// At most kStreamMaxWaves waves per workgroup (the launcher's rule; the rings
+// of 16 rows fit no more), so each may take up to 256 registers.
+constexpr int kStreamMaxWaves = 8;
 
 template <int ROWS, int RING, bool AGROUP>
-__global__ __launch_bounds__(kGemvMaxWaves * 64) void gemv_stream_kernel(
+__global__ __launch_bounds__(kStreamMaxWaves * 64) void gemv_stream_kernel(
     const int8_t *__restrict__ a, const int8_t *w, const float *__restrict__ a_s,
     const float *__restrict__ w_s, uint16_t *__restrict__ out, uint32_t m, uint32_t n, uint32_t k,
     uint32_t a_ld, uint32_t a_shift, uint32_t cpw) {
     using Buf = StreamBuf<ROWS>;
-    constexpr int NC = stream_copies<ROWS, AGROUP>();
+    using Copies = StreamCopies<ROWS, AGROUP>;
+    constexpr int NC = Copies::kTotal;
+    constexpr int RT = (ROWS + 15) / 16;  // 16-row MFMA tiles
     static_assert(NC * (RING - 1) < 64, "the copies in flight fit the vmcnt range");
-    static_assert(ROWS <= 16, "one 16-row MFMA tile");
+    static_assert(ROWS <= kGemvStreamMaxRows && (ROWS <= 16 || ROWS % 16 == 0), "whole 16-row tiles");
     extern __shared__ __attribute__((aligned(1024))) int8_t smem[];
 
     const int lane = threadIdx.x & 63;
@@ -643,16 +652,11 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void gemv_stream_kernel(
     Buf *ring = reinterpret_cast<Buf *>(smem) + wave * RING;
 
     // Copy lane roles: byte copies take row (lane / 16) of a 4-row group and
-    // LDS slot lane % 16, fetching chunk slot ^ row; the 16-byte scale copy
-    // takes row lane / 2 (weight rows, then per-block activation rows) and
+    // LDS slot lane % 16, fetching chunk slot ^ row; a 16-byte scale copy takes
+    // row 32 i + lane / 2 (weight rows, then per-block activation rows) and
     // half lane % 2; a 4-byte grouped-scale copy takes activation row
     // 8 i + lane / 8 and block lane % 8.
     const uint32_t slot = lane & 15;
-    const uint32_t srow = lane >> 1;
-    const bool s_live = srow < (uint32_t)(AGROUP ? kGemvCols : kGemvCols + ROWS);
-    const float *s_src = srow < (uint32_t)kGemvCols
-                             ? w_s + (uint64_t)min(n0 + srow, n - 1) * nb
-                             : a_s + (uint64_t)min(srow - kGemvCols, m - 1) * a_ld;
     auto issue = [&](int bi, uint32_t chunk) {
         Buf &b = ring[bi];
         const uint32_t kb = (c_begin + chunk) * kStreamChunkBlocks;
@@ -668,55 +672,65 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void gemv_stream_kernel(
             const int8_t *src = a + (uint64_t)min(r, m - 1) * k + kb * 32 + ((slot ^ (r & 15)) << 4);
             __builtin_amdgcn_global_load_lds(src, (lds_void *)(b.a + i * 1024), 16, 0, 0);
         }
-        if (s_live)
-            __builtin_amdgcn_global_load_lds(s_src + kb + 4 * (lane & 1), (lds_void *)(&b.s[0][0]), 16, 0, 0);
-        if constexpr (AGROUP) {
+        constexpr uint32_t s16_rows = AGROUP ? kGemvCols : kGemvCols + ROWS;
 #pragma unroll
-            for (int i = 0; i < (ROWS * kStreamChunkBlocks + 63) / 64; ++i) {
-                const uint32_t r = 8 * i + (lane >> 3);
-                if (r < (uint32_t)ROWS)
-                    __builtin_amdgcn_global_load_lds(a_s + (uint64_t)min(r, m - 1) * a_ld + ((kb + (lane & 7)) >> a_shift),
-                                                     (lds_void *)(&b.s[kGemvCols + 8 * i][0]), 4, 0, 0);
-            }
+        for (int i = 0; i < Copies::kScale16; ++i) {
+            const uint32_t srow = 32 * i + (lane >> 1);
+            const float *src = srow < (uint32_t)kGemvCols
+                                   ? w_s + (uint64_t)min(n0 + srow, n - 1) * nb
+                                   : a_s + (uint64_t)min(srow - kGemvCols, m - 1) * a_ld;
+            if (srow < s16_rows)
+                __builtin_amdgcn_global_load_lds(src + kb + 4 * (lane & 1), (lds_void *)(&b.s[32 * i][0]), 16, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < Copies::kScale4; ++i) {
+            const uint32_t r = 8 * i + (lane >> 3);
+            if (r < (uint32_t)ROWS)
+                __builtin_amdgcn_global_load_lds(a_s + (uint64_t)min(r, m - 1) * a_ld + ((kb + (lane & 7)) >> a_shift),
+                                                 (lds_void *)(&b.s[kGemvCols + 8 * i][0]), 4, 0, 0);
         }
     };
 
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    const uint32_t arow = min(c16, (uint32_t)ROWS - 1);
+    float acc[RT][4];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
+    uint32_t arow[RT];  // LDS activation row of this lane in tile t
+#pragma unroll
+    for (int t = 0; t < RT; ++t) arow[t] = min(16u * t + c16, (uint32_t)ROWS - 1);
     auto compute = [&](int bi) {
         const Buf &b = ring[bi];
         const int8_t *wr = b.w + c16 * kStreamRowBytes;
-        const int8_t *ar = b.a + arow * kStreamRowBytes;
         auto off = [&](uint32_t r, int blk) {  // byte offset of this lane's 8 bytes of a block
             return ((((uint32_t)(2 * blk) + (q >> 1)) ^ (r & 15)) << 4) + 8 * (q & 1);
         };
         const v4i zero4 = {0, 0, 0, 0};
         const v16f zero16 = {};
-        ChainOps x[2];
-        auto read = [&](ChainOps &o, int i) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                o.av[j] = *reinterpret_cast<const long *>(ar + off(arow, 4 * i + j));
-                o.wv[j] = *reinterpret_cast<const long *>(wr + off(c16, 4 * i + j));
-            }
-            o.as = b.s[kGemvCols + arow][4 * i + q];
-            o.ws = b.s[c16][4 * i + q];
-        };
-        read(x[0], 0);
 #pragma unroll
         for (int i = 0; i < kStreamChunkBlocks / 4; ++i) {
-            if (i + 1 < kStreamChunkBlocks / 4) read(x[(i + 1) & 1], i + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            const ChainOps &cur = x[i & 1];
-            v4i p[4];
+            long wv[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(cur.av[j], cur.wv[j], zero4, 0, 0, 0);
-            const v16f sc = __builtin_amdgcn_mfma_f32_16x16x1f32(cur.as, cur.ws, zero16, 0, 0, 0);
+            for (int j = 0; j < 4; ++j) wv[j] = *reinterpret_cast<const long *>(wr + off(c16, 4 * i + j));
+            const float ws = b.s[c16][4 * i + q];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int t = 0; t < RT; ++t) {
+                const int8_t *ar = b.a + arow[t] * kStreamRowBytes;
+                long av[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] = fmaf((float)p[j][r], sc[4 * j + r], acc[r]);
-            __builtin_amdgcn_sched_barrier(0);
+                for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const long *>(ar + off(arow[t], 4 * i + j));
+                const float as = b.s[kGemvCols + arow[t]][4 * i + q];
+                v4i p[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av[j], wv[j], zero4, 0, 0, 0);
+                // the 4 blocks' scale outer products a_s x w_s, one rounded
+                // product per output: block j in registers 4j..4j+3, laid out like P
+                const v16f sc = __builtin_amdgcn_mfma_f32_16x16x1f32(as, ws, zero16, 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[t][r] = fmaf((float)p[j][r], sc[4 * j + r], acc[t][r]);
+            }
         }
     };
     auto reads_done = [&]() {
@@ -745,8 +759,30 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void gemv_stream_kernel(
             reads_done();
         }
     }
+
+    // Per tile: the waves' partial sums added in wave order (alternating
+    // between two LDS buffers, so one barrier per tile suffices).
     __syncthreads();  // every wave is done with its ring
-    gemv_reduce_store(reinterpret_cast<float *>(smem), acc, wave, nwaves, lane, n0, m, n, out);
+    float *red = reinterpret_cast<float *>(smem);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        float *rb = red + (t & 1) * (kGemvMaxWaves * 64 * 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rb[(wave * 64 + lane) * 4 + r] = acc[t][r];
+        __syncthreads();
+        if (wave == t % nwaves) {
+            float tot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int v = 0; v < nwaves; ++v)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) tot[r] += rb[(v * 64 + lane) * 4 + r];
+            const uint32_t col = n0 + c16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t row = 16 * t + 4 * q + r;
+                if (row < m && col < n) out[(uint64_t)row * n + col] = f32_to_bf16_rne(tot[r]);
+            }
+        }
+    }
 }
 
 }  // namespace
@@ -810,12 +846,14 @@ hipError_t launch_stream(const int8_t *a_i8, const int8_t *w_i8, const float *a_
     constexpr int kRing = 2;
     const uint32_t tiles = (uint32_t)div_up(n, kGemvCols);
     const uint32_t nchunks = k / 32 / kStreamChunkBlocks;
-    uint32_t waves = tiles >= 1024 ? 4u : max(2u, min(8u, 2048u / tiles));
-    waves = min(waves, nchunks);
+    constexpr uint32_t ring_bytes = kRing * sizeof(StreamBuf<ROWS>);
+    constexpr uint32_t max_waves = kLdsBytes / ring_bytes;  // 8 up to 16 rows, 3 at 64
+    static_assert(max_waves >= 3, "three waves' rings fit in LDS");
+    uint32_t waves = tiles >= 1024 ? 4u : max(2u, min((uint32_t)kStreamMaxWaves, 2048u / tiles));
+    waves = min(min(waves, max_waves), nchunks);
     const uint32_t cpw = (uint32_t)div_up(nchunks, waves);
     waves = (uint32_t)div_up(nchunks, cpw);
-    const uint32_t lds = max(waves * kRing * (uint32_t)sizeof(StreamBuf<ROWS>), kRedBytes);
-    static_assert(8 * kRing * sizeof(StreamBuf<16>) <= kLdsBytes, "eight waves' rings fit in LDS");
+    const uint32_t lds = max(waves * ring_bytes, (ROWS > 16 ? 2 : 1) * kRedBytes);
     hipLaunchKernelGGL((gemv_stream_kernel<ROWS, kRing, AGROUP>), dim3(tiles), dim3(64 * waves), lds, s, a_i8, w_i8,
                        a_scale, w_scale, out, m, n, k, a_ld, a_shift, cpw);
     return hipGetLastError();
@@ -829,7 +867,10 @@ hipError_t launch_stream_rows(const int8_t *a_i8, const int8_t *w_i8, const floa
     if (m <= 2) return launch_stream<2, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
     if (m <= 4) return launch_stream<4, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
     if (m <= 8) return launch_stream<8, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
-    return launch_stream<16, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+    if (m <= 16) return launch_stream<16, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+    if (m <= 32) return launch_stream<32, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+    if (m <= 48) return launch_stream<48, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+    return launch_stream<64, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
 }
 
 }  // namespace
@@ -837,7 +878,7 @@ hipError_t launch_stream_rows(const int8_t *a_i8, const int8_t *w_i8, const floa
 hipError_t launch_gemv(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
                        uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
                        uint32_t k, hipStream_t s) {
-    if (k % (32 * kStreamChunkBlocks) == 0) {
+    if (k % kGemvStreamKAlign == 0) {
         if (a_shift) return launch_stream_rows<true>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
         return launch_stream_rows<false>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
     }

@@ -102,8 +102,9 @@ int requant_a_int8(const uint16_t *a_bf16, int8_t *a_i8, float *a_scale,
  * summation order is the kernel's own (not part of the contract); the result
  * is within 4e-3 relative or 1 BF16 ulp of the FP64 value, or within the
  * worst-case FP32 error of a K/32-term sum where that is larger.
- * m <= 16 (one 16-row matrix-core tile) runs the weight-streaming GEMV, m > 16
- * the MFMA GEMM.
+ * m <= 16 (one 16-row matrix-core tile) runs the weight-streaming GEMV; so
+ * does m <= 48 when k is a multiple of 256 and n <= 4096 (16-column
+ * workgroups at most one per CU); other shapes run the MFMA GEMM.
  * Errors: BSR_EINVAL, BSR_ENULL, BSR_EALIGN, BSR_EDEVICE, BSR_ELAUNCH.
  */
 int int8_gemm_blockscaled(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
@@ -112,9 +113,10 @@ int int8_gemm_blockscaled(const int8_t *a_i8, const int8_t *w_i8, const float *a
 
 /* Paths of int8_gemm_blockscaled_ex. */
 enum bsr_path {
-    BSR_PATH_AUTO = 0, /* GEMV iff m <= 16, as int8_gemm_blockscaled    */
+    BSR_PATH_AUTO = 0, /* as int8_gemm_blockscaled                       */
     BSR_PATH_GEMM = 1, /* the MFMA GEMM at any m                         */
-    BSR_PATH_GEMV = 2, /* the GEMV; requires m <= 16, else BSR_EINVAL    */
+    BSR_PATH_GEMV = 2, /* the GEMV; requires m <= 16, or m <= 64 with k a
+                        * multiple of 256, else BSR_EINVAL              */
     BSR_PATH_INVARIANT = 3 /* m <= 16: a GEMV that accumulates every output
                             * over the K blocks in increasing order, as the
                             * GEMM does; m > 16: the GEMM.  A row's output

@@ -108,7 +108,11 @@ def test_bad_scale2_and_path():
     assert L.int8_gemm_blockscaled_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 64, None, 4) == bsr.BSR_EINVAL
     assert L.int8_gemm_blockscaled_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 64, None, -1) == bsr.BSR_EINVAL
     assert L.int8_gemm_blockscaled_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 17, 4, 64, None,
-                                      bsr.PATH_GEMV) == bsr.BSR_EINVAL
+                                      bsr.PATH_GEMV) == bsr.BSR_EINVAL  # m > 16, k % 256 != 0
+    assert L.int8_gemm_blockscaled_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 65, 4, 256, None,
+                                      bsr.PATH_GEMV) == bsr.BSR_EINVAL  # m > 64
+    assert L.int8_gemm_blockscaled_ex(None, FAKE, FAKE, FAKE, FAKE, 64, 4, 256, None,
+                                      bsr.PATH_GEMV) == bsr.BSR_ENULL   # m <= 64, k % 256 == 0: accepted
 
 
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU may be present")
@@ -137,6 +141,7 @@ def test_gemm_agroup_validation():
     assert L.int8_gemm_blockscaled_agroup(*args, 128, FAKE, FAKE, 4, 4, 96, None, 0) == bsr.BSR_EINVAL
     assert L.int8_gemm_blockscaled_agroup(*args, 0, FAKE, FAKE, 4, 4, 48, None, 0) == bsr.BSR_EINVAL
     assert L.int8_gemm_blockscaled_agroup(*args, 0, FAKE, FAKE, 17, 4, 96, None, 2) == bsr.BSR_EINVAL  # gemv m>16
+    assert L.int8_gemm_blockscaled_agroup(*args, 0, FAKE, FAKE, 65, 4, 256, None, 2) == bsr.BSR_EINVAL  # gemv m>64
     assert L.int8_gemm_blockscaled_agroup(*args, 0, FAKE, FAKE, 4, 4, 96, None, 7) == bsr.BSR_EINVAL  # path
     assert L.int8_gemm_blockscaled_agroup(*args, 128, FAKE, FAKE, 0, 4, 256, None, 0) == bsr.BSR_OK
     assert L.int8_gemm_blockscaled_agroup(FAKE, FAKE, None, 128, FAKE, FAKE, 4, 4, 256, None, 0) == bsr.BSR_ENULL

@@ -122,7 +122,8 @@ def _grouped_case(name, a_bits, packed, e4m3, scale2, group, path, rows=None):
                                         (129, 200, 4096, bsr.PATH_GEMM), (1, 333, 4096, bsr.PATH_GEMV),
                                         (5, 333, 1152, bsr.PATH_GEMV), (8, 200, 2176 + 128, bsr.PATH_GEMV),
                                         (3, 100, 16384, bsr.PATH_GEMV), (8, 64, 16384, bsr.PATH_GEMV),
-                                        (2, 90, 1056, bsr.PATH_GEMV), (16, 130, 2048, bsr.PATH_GEMV)])
+                                        (2, 90, 1056, bsr.PATH_GEMV), (16, 130, 2048, bsr.PATH_GEMV),
+                                        (40, 300, 2048, bsr.PATH_GEMV), (64, 77, 4096, bsr.PATH_GEMV)])
 def test_grouped_gemm_parity(m, n, k, path, group):
     if group == 128 and k % 128:
         pytest.skip("k not a multiple of 128")

@@ -75,6 +75,21 @@ def test_gemv_parity_random_and_against_gemm(m, k):
     assert np.all(np.abs(dv - dg) <= np.maximum(bf16_ulp(dv), bf16_ulp(dg)))
 
 
+# The streamed GEMV over two to four 16-row tiles (K a multiple of 256): every
+# tile count, ragged last tiles and columns, one chunk per wave (K = 256) and
+# long K; the automatic path takes the GEMV for m <= 48 on these narrow grids
+# and the GEMM for (64, 257, 4096).
+@pytest.mark.parametrize("m,n,k", [(17, 333, 256), (24, 300, 2048), (32, 4096, 4096), (33, 200, 14336),
+                                   (48, 1000, 1024), (49, 130, 512), (64, 257, 4096)])
+def test_gemv_multi_tile_parity(m, n, k):
+    say(f"gemv multi-tile m={m} n={n} k={k}")
+    a, w, a_s, w_s = _rand_operands(500 + m, m, n, k, zero_frac=0.05)
+    y, t = oracle.gemm_ref(a, w, a_s, w_s)
+    da, dw, das, dws = to_dev(a), to_dev(w), to_dev(a_s), to_dev(w_s)
+    _check(f"gemv {m}x{n}x{k}", host(gpu_gemm(da, dw, das, dws, path=bsr.PATH_GEMV)), y, t, k)
+    _check(f"auto {m}x{n}x{k}", host(gpu_gemm(da, dw, das, dws, path=bsr.PATH_AUTO)), y, t, k)
+
+
 def test_gemm_exact_power_of_two_bit_equal():
     # Power-of-two scales and small codes: every FP32 step is exact, so the output
     # must be the BF16 rounding of the exact integer result, bit for bit.
