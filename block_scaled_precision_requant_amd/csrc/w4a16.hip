@@ -4,12 +4,16 @@
 // GEMV: BF16 activations times an NVFP4 weight (packed E2M1, one E4M3 scale
 // per 16 elements, one F32 scale_2).  Result definition used here:
 //   out[i, j] = bf16_rne( fl32( S[i, j] * scale_2 ) ),
-//   S[i, j]   = FP32 sum over k of x[i, k] * (e2m1[j, k] * s16[j, k / 16]),
-// where every product is exact (e2m1 * s16 has at most 6 significant bits, so
-// it is a BF16 value, and BF16 x BF16 is exact in FP32); only the FP32 sum
-// (order: the kernel's own) and the two final roundings are inexact.
+//   S[i, j]   = an FP32 evaluation of the sum over k of x[i, k] * e2m1[j, k] *
+//               s16[j, k / 16] (order: the kernel's own).
+// Two kernels.  The streamed one (K a multiple of 256, below) sums the exact
+// products x * e2m1 per 16-element block and adds s16 times each block sum;
+// the register-decode one sums the exact products x * (e2m1 * s16) (e2m1 *
+// s16 has at most 6 significant bits, a BF16 value, and BF16 x BF16 is exact
+// in FP32).  Either way only FP32 sums, one product per block or none, and
+// the two final roundings are inexact.
 //
-// Mapping.  Workgroup = 16 output columns x all of K, K split over its waves
+// Register-decode kernel mapping.  Workgroup = 16 output columns x all of K, K split over its waves
 // in super-steps of 128.  In a super-step lane l (column c = l % 16, quarter
 // q = l / 16) owns K range [128 T + 32 q, +32): it loads those 16 packed bytes
 // of weight row n0 + c (16 rows x 64 contiguous bytes per instruction), turns
@@ -267,10 +271,216 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void w4a16_kernel(
     }
 }
 
+// ---------------------------------------------------------------- stream
+
+// Streamed W4A16 (K a multiple of 256).  Same workgroup shape (16 columns,
+// K split over the waves); each wave brings its run of 256-element chunks --
+// 16 weight rows of packed codes, their E4M3 codes and the activation rows --
+// through a private 2-buffer LDS ring with global_load_lds.  Per 16-element
+// scale block: the lane's 4 codes become BF16 E2M1 values through
+// v_cvt_scalef32_pk_bf16_fp4 (scale 1, exact), one v_mfma_f32_16x16x16bf16_1k
+// gives the block's FP32 partial sums P (products exact, 16 terms), and the
+// accumulators take fma(P, s16, acc) with s16 from v_cvt_f32_fp8 (OCP E4M3,
+// exact).  So S[i, j] = FP32 sum over blocks of s16 * (FP32 sum over the block
+// of x * e2m1): the same real value as the sum over k of x * (e2m1 * s16),
+// evaluated in another FP32 order (within the K + 16 term bound).
+constexpr int kW4ChunkK = 256;
+constexpr int kW4ChunkBlocks = kW4ChunkK / 16;
+constexpr int kW4WRowBytes = kW4ChunkK / 2;  // 128: 8 slots of 16 bytes
+constexpr int kW4ARowBytes = kW4ChunkK * 2;  // 512: 32 slots of 16 bytes
+constexpr int kW4StreamMaxWaves = 8;
+// LDS rows are unpadded and XOR-swizzled by 16-byte slot: slot s of weight row
+// r holds slot s ^ (r & 7) of the row, slot s of activation row r holds slot
+// s ^ (r & 15), so 16 rows read at one offset spread over the banks.
+template <int ROWS>
+struct W4Buf {
+    static constexpr int kARows = ROWS < 2 ? 2 : ROWS;
+    uint8_t w[kGemvCols * kW4WRowBytes];
+    uint8_t a[kARows * kW4ARowBytes];
+    uint8_t s[kGemvCols * kW4ChunkBlocks];  // E4M3 codes, [row][block]
+};
+template <int ROWS>
+constexpr int w4_stream_copies() {  // copy instructions per chunk
+    return kGemvCols * kW4WRowBytes / 1024 + W4Buf<ROWS>::kARows * kW4ARowBytes / 1024 + 1;
+}
+
+typedef short short4_ __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// OCP E4M3 code in byte b of a dword -> binary32 (v_cvt_f32_fp8, exact; the
+// byte select is an immediate).
+__device__ __forceinline__ float e4m3_byte(uint32_t codes, int b) {
+    switch (b) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)codes, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)codes, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)codes, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8((int)codes, 3);
+    }
+}
+
+// Wait until at most C * later copies are outstanding (later <= N): s_waitcnt
+// takes an immediate, so one branch per count.
+template <int C, int N>
+__device__ __forceinline__ void wait_vm_later(uint32_t later) {
+    if constexpr (N > 0) {
+        if (later == (uint32_t)N) {
+            wait_vm_le<C * N>();
+            return;
+        }
+        wait_vm_later<C, N - 1>(later);
+    } else {
+        wait_vm_le<0>();
+    }
+}
+
+template <int ROWS, int RING>
+__global__ __launch_bounds__(kW4StreamMaxWaves * 64) void w4a16_stream_kernel(
+    const uint16_t *__restrict__ x, const uint8_t *wp, const uint8_t *we, float scale2,
+    uint16_t *__restrict__ out, uint32_t m, uint32_t n, uint32_t k, uint32_t cpw) {
+    using Buf = W4Buf<ROWS>;
+    constexpr int NC = w4_stream_copies<ROWS>();
+    static_assert(NC * (RING - 1) < 64, "the copies in flight fit the vmcnt range");
+    static_assert(ROWS <= kGemvMaxRows, "one 16-row MFMA tile");
+    extern __shared__ __attribute__((aligned(1024))) int8_t smem[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nwaves = blockDim.x >> 6;
+    const int q = lane >> 4;
+    const uint32_t c16 = lane & 15;
+    const uint32_t n0 = blockIdx.x * kGemvCols;
+    const uint32_t c_begin = wave * cpw;
+    const uint32_t nchunks = min(k / kW4ChunkK, c_begin + cpw) - c_begin;  // >= 1
+    Buf *ring = reinterpret_cast<Buf *>(smem) + wave * RING;
+
+    auto issue = [&](int bi, uint32_t chunk) {
+        Buf &b = ring[bi];
+        const uint32_t kc = (c_begin + chunk) * kW4ChunkK;
+#pragma unroll
+        for (int i = 0; i < kGemvCols * kW4WRowBytes / 1024; ++i) {  // 8 rows x 128 bytes per copy
+            const uint32_t r = 8 * i + (lane >> 3), slot = lane & 7;
+            const uint8_t *src = wp + (uint64_t)min(n0 + r, n - 1) * (k / 2) + kc / 2 + ((slot ^ (r & 7)) << 4);
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(b.w + i * 1024), 16, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < Buf::kARows * kW4ARowBytes / 1024; ++i) {  // 2 rows x 512 bytes per copy
+            const uint32_t r = 2 * i + (lane >> 5), slot = lane & 31;
+            const uint16_t *src = x + (uint64_t)min(r, m - 1) * k + kc + ((slot ^ (r & 15)) << 3);
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(b.a + i * 1024), 16, 0, 0);
+        }
+        if (lane < kGemvCols)  // 16 rows x 16 scale codes
+            __builtin_amdgcn_global_load_lds(we + (uint64_t)min(n0 + lane, n - 1) * (k / 16) + kc / 16,
+                                             (lds_void *)b.s, 16, 0, 0);
+    };
+
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t arow = min(c16, (uint32_t)ROWS - 1);
+    const uint32_t wshift = 16 * (q & 1);  // this lane's 2 code bytes within a dword
+    auto compute = [&](int bi) {
+        const Buf &b = ring[bi];
+        const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int g = 0; g < kW4ChunkBlocks / 4; ++g) {
+            const uint32_t scodes = *reinterpret_cast<const uint32_t *>(b.s + c16 * kW4ChunkBlocks + 4 * g);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int j = 4 * g + jj;  // block of the chunk
+                // activations: elements 16 j + 4 q .. + 3 of row arow
+                const uint32_t aslot = (uint32_t)(2 * j) + (q >> 1);
+                const short4_ av = *reinterpret_cast<const short4_ *>(
+                    b.a + arow * kW4ARowBytes + ((aslot ^ (arow & 15)) << 4) + 8 * (q & 1));
+                // weights: code bytes 2 q, 2 q + 1 of block j of row c16
+                const uint32_t wslot = (uint32_t)j >> 1;
+                const uint32_t wd = *reinterpret_cast<const uint32_t *>(
+                    b.w + c16 * kW4WRowBytes + ((wslot ^ (c16 & 7)) << 4) + 8 * (j & 1) + 4 * (q >> 1));
+                const uint32_t wb = wd >> wshift;
+                const auto w01 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wb, 1.0f, 0);
+                const auto w23 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wb, 1.0f, 1);
+                const u32x2 wpair = {__builtin_bit_cast(uint32_t, w01), __builtin_bit_cast(uint32_t, w23)};
+                const short4_ wv = __builtin_bit_cast(short4_, wpair);  // elements 4q .. 4q + 3
+                const v4f p = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, wv, zero4, 0, 0, 0);
+                const float sc = e4m3_byte(scodes, jj);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = fmaf(p[r], sc, acc[r]);
+            }
+        }
+    };
+    auto reads_done = [&]() {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+    };
+
+    // Chunks c + 1 .. c + RING - 1 are in flight while chunk c is computed.
+#pragma unroll
+    for (int r = 0; r < RING - 1; ++r)
+        if ((uint32_t)r < nchunks) issue(r, r);
+    for (uint32_t c0 = 0; c0 < nchunks; c0 += RING) {
+#pragma unroll
+        for (int u = 0; u < RING; ++u) {
+            const uint32_t c = c0 + u;
+            if (c >= nchunks) break;
+            // buffer (u + RING - 1) % RING held chunk c - 1, whose reads are done
+            if (c + RING - 1 < nchunks) issue((u + RING - 1) % RING, c + RING - 1);
+            wait_vm_later<NC, RING - 1>(min(nchunks - 1 - c, (uint32_t)RING - 1));
+            asm volatile("" ::: "memory");
+            compute(u);
+            reads_done();
+        }
+    }
+
+    // partial sums of the waves, added in wave order; then scale_2 and BF16
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(smem);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[(wave * 64 + lane) * 4 + r] = acc[r];
+    __syncthreads();
+    if (wave == 0) {
+        float tot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int v = 0; v < nwaves; ++v)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tot[r] += red[(v * 64 + lane) * 4 + r];
+        const uint32_t oc = n0 + c16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t row = 4 * q + r;
+            if (row < m && oc < n) out[(uint64_t)row * n + oc] = f32_to_bf16_rne(tot[r] * scale2);
+        }
+    }
+}
+
+template <int ROWS, int RING = 2>
+hipError_t launch_w4a16_stream(const uint16_t *x, const uint8_t *w_packed, const uint8_t *w_e4m3, float scale2,
+                               uint16_t *out, uint32_t m, uint32_t n, uint32_t k, hipStream_t s) {
+    constexpr uint32_t ring_bytes = RING * sizeof(W4Buf<ROWS>);
+    constexpr uint32_t lds_waves = 160u * 1024u / ring_bytes;
+    constexpr uint32_t max_waves = lds_waves < (uint32_t)kW4StreamMaxWaves ? lds_waves : kW4StreamMaxWaves;
+    const uint32_t tiles = (uint32_t)div_up(n, kGemvCols);
+    const uint32_t nchunks = k / kW4ChunkK;
+    // as many waves (2 to 8) as let the workgroups a CU must run share its LDS
+    // at once (measured: N = 14336 wants 8 waves at m <= 2 but 2 at m = 8)
+    const uint32_t wg_per_cu = (uint32_t)div_up(tiles, kGemmCus);
+    uint32_t waves = max(2u, (160u * 1024u / wg_per_cu) / ring_bytes);
+    waves = min(min(waves, max_waves), nchunks);
+    const uint32_t cpw = (uint32_t)div_up(nchunks, waves);
+    waves = (uint32_t)div_up(nchunks, cpw);
+    const uint32_t lds = max(waves * ring_bytes, (uint32_t)(kW4StreamMaxWaves * 64 * 4 * 4));
+    hipLaunchKernelGGL((w4a16_stream_kernel<ROWS, RING>), dim3(tiles), dim3(64 * waves), lds, s, x, w_packed, w_e4m3,
+                       scale2, out, m, n, k, cpw);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_w4a16(const uint16_t *x, const uint8_t *w_packed, const uint8_t *w_e4m3, float scale2,
                         uint16_t *out, uint32_t m, uint32_t n, uint32_t k, hipStream_t s) {
+    if (k % kW4ChunkK == 0) {
+        if (m <= 1) return launch_w4a16_stream<1>(x, w_packed, w_e4m3, scale2, out, m, n, k, s);
+        if (m <= 2) return launch_w4a16_stream<2>(x, w_packed, w_e4m3, scale2, out, m, n, k, s);
+        if (m <= 4) return launch_w4a16_stream<4>(x, w_packed, w_e4m3, scale2, out, m, n, k, s);
+        if (m <= 8) return launch_w4a16_stream<8>(x, w_packed, w_e4m3, scale2, out, m, n, k, s);
+        return launch_w4a16_stream<16>(x, w_packed, w_e4m3, scale2, out, m, n, k, s);
+    }
+    // Other K: the register-decode kernel.
     // Column tiles per workgroup: two from m = 4 on, where the activation
     // bytes a workgroup stages (2 m per K element) approach the weight bytes
     // of one 16-column tile (9 per K element) -- if that still leaves a

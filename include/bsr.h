@@ -166,10 +166,13 @@ int silu_mul_requant_int8(const uint16_t *gate, const uint16_t *up, uint32_t ld,
  *   w_packed [n, k/2]  u8 (E2M1 pairs, low nibble first), 16-byte aligned
  *   w_e4m3   [n, k/16] u8, 16-byte aligned when k % 256 == 0, else 2-byte
  *   out      [m, n]    BF16 as raw u16, 2-byte aligned
- * out[i,j] = bf16_rne( fl32( S * scale2 ) ), S = FP32 sum over k of
- * x[i,k] * e2m1[j,k] * s16[j,k/16] (each product exact; the summation order
- * is the kernel's own): within 4e-3 relative or 1 BF16 ulp of the FP64 value,
- * or within the worst-case FP32 error of a (k + 16)-term sum.
+ * out[i,j] = bf16_rne( fl32( S * scale2 ) ), S an FP32 evaluation of the sum
+ * over k of x[i,k] * e2m1[j,k] * s16[j,k/16] in the kernel's own order (for
+ * k % 256 == 0 the exact products x * e2m1 are summed per 16-element scale
+ * block and each block sum is multiplied by its s16; otherwise the exact
+ * products x * (e2m1 * s16) are summed): within 4e-3 relative or 1 BF16 ulp
+ * of the FP64 value, or within the worst-case FP32 error of a (k + 16)-term
+ * sum.
  * Errors: BSR_EINVAL (k, m > 16, scale2 not finite), BSR_ENULL, BSR_EALIGN,
  * BSR_EDEVICE, BSR_ELAUNCH.
  */

@@ -66,6 +66,23 @@ def test_exact_power_of_two_bit_equal():
     assert np.array_equal(out, exp_bits), f"{np.sum(out != exp_bits)} mismatches"
 
 
+# Every finite E4M3 scale code -- signs, zeros, subnormals, non-powers of two
+# up to 448 -- with every E2M1 code, through both kernels (K = 2048 streamed,
+# decoding the scale with the hardware conversion; K = 1056 register decode).
+@pytest.mark.parametrize("k", [2048, 1056])
+def test_all_finite_scale_codes(k):
+    rng = np.random.default_rng(k)
+    m, n = 5, 200
+    x = inputs.bf16_normal(rng, m, k)
+    wp = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    we = finite[rng.integers(0, finite.size, size=(n, k // 16))]
+    we.flat[:finite.size] = finite  # each code at least once
+    y, t = oracle.w4a16_ref(x, wp, we, inputs.SCALE2_1_448)
+    out = host(gpu_w4a16(x, wp, we, inputs.SCALE2_1_448))
+    _check(f"w4a16 all scale codes k={k}", out, y, t, k)
+
+
 def test_rows_independent_of_m():
     rng = np.random.default_rng(4)
     k, n = 2048, 97
