@@ -31,9 +31,11 @@ __device__ __forceinline__ float quad_max(float x) {
     return x;
 }
 
+// Low bytes of a, b, c, d (two's complement codes) packed in that order.
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
-    return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
-           ((uint32_t)d << 24);
+    const uint32_t ab = __builtin_amdgcn_perm((uint32_t)b, (uint32_t)a, 0x0C0C0400u);  // [a, b, 0, 0]
+    const uint32_t cd = __builtin_amdgcn_perm((uint32_t)d, (uint32_t)c, 0x0C0C0400u);  // [c, d, 0, 0]
+    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);                                 // [a, b, c, d]
 }
 
 __device__ __forceinline__ float local_amax(const float (&v)[8]) {
@@ -57,17 +59,19 @@ __device__ __forceinline__ uint2 int8_codes(const float (&v)[8], float s) {
         const bool pow2 = (sb & 0x007FFFFFu) == 0;
         const float r = pow2 ? __uint_as_float(0x7F000000u - (sb & 0x7F800000u))
                              : __builtin_amdgcn_rcpf(s);
-        uint32_t near = 0;
+        // largest distance of a quotient from its rounding: only when some
+        // element is within 2^-14 of a half-integer is the divide needed
+        float dev = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float q0 = v[i] * r;
             t[i] = rintf(q0);
-            near |= (fabsf(q0 - t[i]) > kTieGuard) ? (1u << i) : 0u;
+            dev = fmaxf(dev, fabsf(q0 - t[i]));
         }
-        if (!pow2 && near) {
+        if (!pow2 && dev > kTieGuard) {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                if (near & (1u << i)) t[i] = rintf(v[i] / s);
+                if (fabsf(v[i] * r - t[i]) > kTieGuard) t[i] = rintf(v[i] / s);
         }
     }
     return make_uint2(pack4_i8((int)t[0], (int)t[1], (int)t[2], (int)t[3]),
@@ -169,9 +173,12 @@ __device__ __forceinline__ uint32_t silu_mul_bf16(uint32_t g_bits, uint32_t u_bi
 //   |g| < 2^-25:  exp(-g) rounds to 1, so silu32(g) = g / 2 (exact, = g * 0.5);
 //   g >= 32:      1 + exp(-g) rounds to 1, so silu32(g) = g;
 //   g <= -128:    exp(-g) overflows binary32, so silu32(g) = g / inf = -0.
-// The band -- positive gates with exponent -25..4, negative ones with -25..6 --
-// is 62 binades x 128 BF16 values, tabulated with silu32 itself.
-constexpr int kSiluPosBinades = 30, kSiluNegBinades = 32;
+// The band -- gates of either sign with exponent -25..6 -- is 64 binades x 128
+// BF16 values, tabulated with silu32 itself (the positive gates from 32 up
+// hold silu32(g) = g like the closed form).  Within it the index is a bit
+// field of the gate: magnitude minus the band's lowest key in bits 0-11, sign
+// in bit 12.
+constexpr int kSiluPosBinades = 32, kSiluNegBinades = 32;
 constexpr int kSiluTable = (kSiluPosBinades + kSiluNegBinades) * 128;
 constexpr uint32_t kSiluLoExp = 127 - 25;  // biased exponent of the band's lowest binade
 
@@ -197,20 +204,45 @@ __device__ __forceinline__ float silu_lookup(uint32_t b, const float *tab) {
     return key < lo ? g * 0.5f : (key >= hi ? outer : t);
 }
 
-// binary32 -> the nearest BF16 value (ties to even), kept as a binary32.
-__device__ __forceinline__ float round_bf16(float x) {
-    const uint32_t u = __float_as_uint(x);
-    return __uint_as_float((u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u);
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-// SiLU(gate) * up of one chunk, rounded to BF16 values.
+// SiLU(gate) * up of one chunk, rounded to BF16 values (v_cvt_pk_bf16_f32:
+// round to nearest even, as f32_to_bf16_rne on every non-NaN value; a NaN
+// stays a NaN, which the quantizer treats alike whatever its payload).  Every gate
+// in the band reads its table entry at the bit-field index; a lane holding a
+// gate outside it redoes its chunk with silu_lookup.
 __device__ __forceinline__ void silu_mul_chunk(uint4 gr, uint4 ur, const float *tab, float (&h)[8]) {
+    constexpr uint32_t lo = kSiluLoExp << 7, band = kSiluPosBinades * 128;
+    static_assert(kSiluPosBinades == kSiluNegBinades && band == 4096, "index = 12 bits of magnitude + sign");
     const uint32_t gw[4] = {gr.x, gr.y, gr.z, gr.w};
     const uint32_t uw[4] = {ur.x, ur.y, ur.z, ur.w};
+    uint32_t b[8];
+    float u[8], sv[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // element 2i in the low half of word i
-        h[2 * i] = round_bf16(silu_lookup(gw[i] & 0xFFFFu, tab) * __uint_as_float(uw[i] << 16));
-        h[2 * i + 1] = round_bf16(silu_lookup(gw[i] >> 16, tab) * __uint_as_float(uw[i] & 0xFFFF0000u));
+        b[2 * i] = gw[i] & 0xFFFFu;
+        b[2 * i + 1] = gw[i] >> 16;
+        u[2 * i] = __uint_as_float(uw[i] << 16);
+        u[2 * i + 1] = __uint_as_float(uw[i] & 0xFFFF0000u);
+    }
+    uint32_t off = 0;  // largest (magnitude - lo) mod 2^15: >= band iff some gate is outside
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t d = b[e] - lo;
+        off = max(off, d & 0x7FFFu);
+        sv[e] = tab[(d & (band - 1)) | ((b[e] >> 3) & band)];
+    }
+    if (off >= band) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sv[e] = silu_lookup(b[e], tab);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x2_t p = {sv[2 * i] * u[2 * i], sv[2 * i + 1] * u[2 * i + 1]};
+        const uint32_t r = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2_t));
+        h[2 * i] = __uint_as_float(r << 16);
+        h[2 * i + 1] = __uint_as_float(r & 0xFFFF0000u);
     }
 }
 
