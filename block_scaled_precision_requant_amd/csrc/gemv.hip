@@ -699,38 +699,57 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void gemv_stream_kernel(
     uint32_t arow[RT];  // LDS activation row of this lane in tile t
 #pragma unroll
     for (int t = 0; t < RT; ++t) arow[t] = min(16u * t + c16, (uint32_t)ROWS - 1);
+    // Operands of 4 blocks: this lane's 8 bytes of each block for its weight
+    // row and activation rows, and the scale pair it feeds the scale-product
+    // MFMA with (block l / 16 of the 4).
+    struct Ops {
+        long wv[4], av[RT][4];
+        float ws, as[RT];
+    };
     auto compute = [&](int bi) {
         const Buf &b = ring[bi];
         const int8_t *wr = b.w + c16 * kStreamRowBytes;
         auto off = [&](uint32_t r, int blk) {  // byte offset of this lane's 8 bytes of a block
             return ((((uint32_t)(2 * blk) + (q >> 1)) ^ (r & 15)) << 4) + 8 * (q & 1);
         };
-        const v4i zero4 = {0, 0, 0, 0};
-        const v16f zero16 = {};
+        auto read = [&](Ops &o, int i) {
 #pragma unroll
-        for (int i = 0; i < kStreamChunkBlocks / 4; ++i) {
-            long wv[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) wv[j] = *reinterpret_cast<const long *>(wr + off(c16, 4 * i + j));
-            const float ws = b.s[c16][4 * i + q];
+            for (int j = 0; j < 4; ++j) o.wv[j] = *reinterpret_cast<const long *>(wr + off(c16, 4 * i + j));
+            o.ws = b.s[c16][4 * i + q];
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
                 const int8_t *ar = b.a + arow[t] * kStreamRowBytes;
-                long av[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const long *>(ar + off(arow[t], 4 * i + j));
-                const float as = b.s[kGemvCols + arow[t]][4 * i + q];
+                for (int j = 0; j < 4; ++j) o.av[t][j] = *reinterpret_cast<const long *>(ar + off(arow[t], 4 * i + j));
+                o.as[t] = b.s[kGemvCols + arow[t]][4 * i + q];
+            }
+        };
+        const v4i zero4 = {0, 0, 0, 0};
+        const v16f zero16 = {};
+        // the next 4 blocks' LDS reads are issued before the current ones'
+        // arithmetic, so a lone wave (the path-invariant use) hides their latency
+        Ops x[2];
+        read(x[0], 0);
+#pragma unroll
+        for (int i = 0; i < kStreamChunkBlocks / 4; ++i) {
+            if (i + 1 < kStreamChunkBlocks / 4) read(x[(i + 1) & 1], i + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const Ops &cur = x[i & 1];
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
                 v4i p[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av[j], wv[j], zero4, 0, 0, 0);
+                for (int j = 0; j < 4; ++j)
+                    p[j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(cur.av[t][j], cur.wv[j], zero4, 0, 0, 0);
                 // the 4 blocks' scale outer products a_s x w_s, one rounded
                 // product per output: block j in registers 4j..4j+3, laid out like P
-                const v16f sc = __builtin_amdgcn_mfma_f32_16x16x1f32(as, ws, zero16, 0, 0, 0);
+                const v16f sc = __builtin_amdgcn_mfma_f32_16x16x1f32(cur.as[t], cur.ws, zero16, 0, 0, 0);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) acc[t][r] = fmaf((float)p[j][r], sc[4 * j + r], acc[t][r]);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
     auto reads_done = [&]() {
@@ -787,9 +806,52 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void gemv_stream_kernel(
 
 }  // namespace
 
+namespace {
+
+// The path-invariant GEMV through the streamed kernel with one wave per
+// workgroup: that wave walks every chunk in K order, so each output is the
+// single FP32 chain acc = fma(P_b, fl32(a_s * w_s), acc) over b = 0, 1, ...
+// (and the final wave sum adds it to +0, which changes no value: acc is
+// never -0).  Used for grids of more than one workgroup per CU, whose waves
+// then share the CU (N = 14336, K = 4096: 15.5-16 us against 16.5-22 for the
+// chain kernel); with one workgroup per CU the lone wave's arithmetic bounds
+// both kernels and the chain kernel's 1 KB rows measured faster (22-25 us
+// against 27 at N = 4096, K = 14336, even with six chunks in flight).
+template <int ROWS, bool AGROUP>
+hipError_t launch_chain_stream(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
+                               uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
+                               uint32_t k, hipStream_t s) {
+    const uint32_t tiles = (uint32_t)div_up(n, kGemvCols);
+    const uint32_t nchunks = k / kGemvStreamKAlign;
+#define BSR_CHAIN_STREAM(RG)                                                                                      \
+    hipLaunchKernelGGL((gemv_stream_kernel<ROWS, RG, AGROUP>), dim3(tiles), dim3(64),                            \
+                       max((uint32_t)(RG * sizeof(StreamBuf<ROWS>)), kRedBytes), s, a_i8, w_i8, a_scale, w_scale, \
+                       out, m, n, k, a_ld, a_shift, nchunks)
+    BSR_CHAIN_STREAM(4);
+#undef BSR_CHAIN_STREAM
+    return hipGetLastError();
+}
+
+template <bool AGROUP>
+hipError_t launch_chain_stream_rows(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
+                                    uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
+                                    uint32_t k, hipStream_t s) {
+    if (m <= 1) return launch_chain_stream<1, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+    if (m <= 2) return launch_chain_stream<2, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+    if (m <= 4) return launch_chain_stream<4, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+    if (m <= 8) return launch_chain_stream<8, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+    return launch_chain_stream<16, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+}
+
+}  // namespace
+
 hipError_t launch_gemv_chain(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
                              uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
                              uint32_t k, hipStream_t s) {
+    if (k % kGemvStreamKAlign == 0 && div_up(n, kGemvCols) > (uint64_t)kGemmCus) {
+        if (a_shift) return launch_chain_stream_rows<true>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+        return launch_chain_stream_rows<false>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+    }
     const dim3 grid((uint32_t)div_up(n, kGemvCols)), blk(64);
     const uint32_t nb = k / 32;
     if (nb % 4 == 0) {

@@ -95,6 +95,23 @@ def test_invariant_grouped_scales(m, group):
     assert np.array_equal(inv, ref)
 
 
+# Grids of more than one 16-column workgroup per CU (n = 4112: 257 of them,
+# the last one ragged) with K a multiple of 256 take the streamed kernel as
+# one wave per workgroup; its outputs must equal the GEMM's chain bit for bit.
+@pytest.mark.parametrize("group", [32, 128, 0])
+@pytest.mark.parametrize("m,k", [(1, 256), (3, 2048), (9, 512), (16, 4096)])
+def test_invariant_wide_grid(m, k, group):
+    n = 4112
+    say(f"invariant wide grid m={m} n={n} k={k} group={group}")
+    a, packed, e4m3 = _operands(31 * m + k + group, m, n, k)
+    w_i8, w_s = gpu_requant_w(packed, e4m3, inputs.SCALE2_1_448)
+    q, s = gpu_quant_act(a, group)
+    inv = host(gpu_gemm_agroup(q.view(torch.int8), w_i8, s, group, w_s, path=bsr.PATH_INVARIANT))
+    ref = host(gpu_gemm_agroup(_padded(q.view(torch.int8)), w_i8, _padded(s), group, w_s,
+                               path=bsr.PATH_INVARIANT))[:m]
+    assert np.array_equal(inv, ref), np.argwhere(inv != ref)[:5]
+
+
 def test_invariant_tiny_scale_products():
     """Scale products in the binary32 subnormal range and the largest finite
     products: the GEMM's matrix-core product and the GEMV's vector product of
