@@ -7,8 +7,8 @@
  *   2. requant_a_int8        -- per call: BF16 activations -> int8 + F32 per 32;
  *   3. int8_gemm_blockscaled -- int8 x int8 with an exact int32 dot product per
  *      32-wide K block, each block rescaled in FP32 by a_scale * w_scale,
- *      accumulated in FP32 and written as BF16 (an MFMA GEMM for M > 8, a
- *      weight-streaming GEMV for M <= 16).
+ *      accumulated in FP32 and written as BF16 (a weight-streaming GEMV for
+ *      M <= 16, and up to M = 48 on narrow grids; an MFMA GEMM otherwise).
  * The operations are those of page "metrale_model_layers/layers/ops/
  * gemm_dense_int8.rs": the doc comments of `requant_w_nvfp4_int8` and
  * `int8_gemm_faith2_prefill` (the latter's two launches are entry points 2
