@@ -29,11 +29,13 @@ def _weight(rng, n, k, general=True):
     return wp, we
 
 
-# K % 256 == 0 -> 16-byte scale loads; other K -> per-step 2-byte loads, and
-# K % 128 != 0 leaves a partial last super-step.
+# K % 256 == 0 -> the streamed kernel (the last three cases: wide grids, the
+# last column tile ragged); other K -> the register-decode kernel, per-step
+# 2-byte scale loads, and K % 128 != 0 leaves a partial last super-step.
 @pytest.mark.parametrize("m,n,k", [(1, 333, 256), (2, 70, 2048), (8, 129, 4096), (3, 333, 1056),
                                    (5, 40, 96), (7, 16, 4128), (4, 1, 512), (8, 300, 14336),
-                                   (16, 600, 4096), (12, 300, 14336), (9, 70, 1056)])
+                                   (16, 600, 4096), (12, 300, 14336), (9, 70, 1056),
+                                   (4, 8193, 256), (8, 8200, 512), (16, 8200, 1024)])
 def test_random_shapes(m, n, k):
     rng = np.random.default_rng(m * 7919 + n * 31 + k)
     x = inputs.bf16_normal(rng, m, k)
