@@ -11,7 +11,7 @@ import oracle
 from block_scaled_precision_requant_amd import bsr, inputs
 from gpu_util import DEV, f32_bits, gpu_gemm, gpu_gemm_agroup, gpu_quant_act, gpu_requant_a, gpu_requant_w, \
     host, say, to_dev
-from oracle.compare import check_bf16
+from oracle.compare import bf16_bits_to_f64, check_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +42,37 @@ def test_quantize_act_matches_oracle(m, k, group, fmt, e4m3):
     rng = np.random.default_rng(m * 31 + k)
     a = inputs.bf16_student_t(rng, m, k)
     _assert_quant_equal(f"quant m={m} k={k} g={group} e4m3={e4m3}", a, group, fmt, e4m3)
+
+
+def _e4m3_magnitudes():
+    vals = []
+    for c in range(0x7F):  # non-negative codes, NaN excluded
+        e, mt = c >> 3, c & 7
+        vals.append(mt / 8 * 2.0 ** -6 if e == 0 else (1 + mt / 8) * 2.0 ** (e - 7))
+    return np.array(vals)
+
+
+@pytest.mark.parametrize("group", [32, 128, 0])
+def test_quantize_act_e4m3_exact_midpoints(group):
+    """Quotients v / s exactly on E4M3 rounding midpoints (ties to even), with
+    s = 1.5 * 2^j (not a power of two: a quotient formed with an inexact
+    reciprocal could land on either side) and v = midpoint * s a BF16 value;
+    the E4M3 codes must be the IEEE divide's."""
+    rng = np.random.default_rng(11)
+    mag = _e4m3_magnitudes()
+    mids = (mag[:-1] + mag[1:]) / 2
+    k = 512
+    rows = []
+    for j in (-8, -3, 0, 2):
+        s = 1.5 * 2.0 ** j
+        vals = mids * s
+        assert np.array_equal(bf16_bits_to_f64(inputs.f32_to_bf16_bits(vals.astype(np.float32))), vals)
+        for _ in range(4):
+            row = rng.choice(vals, size=k) * rng.choice([-1.0, 1.0], size=k)
+            row[::32] = 448.0 * s  # every group's amax: s = fl32(amax / 448) = 1.5 * 2^j
+            rows.append(row.astype(np.float32))
+    a = inputs.f32_to_bf16_bits(np.stack(rows))
+    _assert_quant_equal(f"e4m3 midpoints g={group}", a, group, bsr.FMT_E4M3, True)
 
 
 @pytest.mark.parametrize("group", [32, 128, 0])
