@@ -15,8 +15,10 @@
 //    s takes the IEEE divide and the clamp for the whole block.
 //  * NVFP4 path: a half-block holds one E4M3 scale, so its 16 elements take at
 //    most 8 magnitudes.  The 7 non-zero magnitudes of each half are quantized
-//    once (same reciprocal fast path, IEEE divide near ties and for subnormal
-//    s), and every element picks its code with a byte permute.
+//    once (same reciprocal fast path; an element worth exactly half the block
+//    max, the common tie, gets its code from one exact FMA residual; other
+//    near ties and subnormal s take the IEEE divide), and every element picks
+//    its code with a byte permute.
 #include "bsr_internal.h"
 
 namespace bsr {
@@ -465,21 +467,58 @@ __device__ __forceinline__ uint2 lookup8(uint32_t w, uint32_t pos_lo, uint32_t p
                       __builtin_amdgcn_perm(od, ev, 0x07030602u));
 }
 
-// Signed int8 code of v = fl32(fl32(mag * s16) * scale2) in a block of scale
-// s != 0: rne(fl32(v / s)), clamped (reachable only for subnormal s).  Normal
-// s uses the reciprocal fast path of the activation kernel: q0 = v * r with
-// r ~ 1/s (exact for a power of two) is within 2^-15 of v / s, so unless q0
-// is within 2^-14 of a half-integer its rounding is the quotient's.
-__device__ __forceinline__ int w_code(float v, float s, float r, bool exact_r, bool sub) {
-    float t;
-    if (sub) {
-        t = fminf(fmaxf(rintf(v / s), -127.0f), 127.0f);
-    } else {
-        const float q0 = v * r;
-        t = rintf(q0);
-        if (!exact_r && fabsf(q0 - t) > kTieGuard) t = rintf(v / s);
+// Codes of the non-zero magnitudes of one half-block: qm[c] (c = 1..7) is the
+// signed int8 code of v_c = fl32(fl32(mag_c * s16) * scale2) in a block of
+// scale s = fl32(amax / 127) != 0, i.e. rne(fl32(v_c / s)), clamped (reachable
+// only for subnormal s).  Normal s uses the reciprocal fast path of the
+// activation kernel (q0 = v * r within 2^-15 of v / s, so away from a
+// half-integer rne(q0) is the answer), with one exception settled exactly:
+//
+//   an element worth exactly half the block max (|v| = amax / 2, the usual
+//   source of ties in E2M1 data, e.g. magnitude 3 under a max of 6) has the
+//   quotient fl32(amax / s) / 2.  As |amax / s - 127| < 2^-17 (s is amax / 127
+//   rounded), fl32(amax / s) is 127 or a neighbour, so the code is 63 when
+//   fl32(amax / s) < 127, i.e. when amax - 127 s < -2^-18 s, and 64 otherwise
+//   (63.5 itself rounds to even).  Both sides of that comparison are exact:
+//   the FMA residual has fewer than 8 significant bits above ulp(s), and the
+//   power-of-two product stays normal for s >= 2^-100 (q_half is only used
+//   there).
+//
+// Any other quotient within 2^-14 of a half-integer sends the half through
+// one branch that recomputes those codes with the IEEE divide.
+__device__ __forceinline__ void half_codes(float s16, float scale2, float amax, float s, float r,
+                                           bool exact_r, bool sub, bool use_half, float q_half,
+                                           int (&qm)[8]) {
+    const float mags[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+    const float half_amax = 0.5f * amax;
+    const float q_half_signed = copysignf(q_half, s16 * scale2);  // every v_c has this sign
+    float v[8], t[8];
+    bool is_half[8], near[8];
+    bool any_near = false;
+#pragma unroll
+    for (int c = 1; c < 8; ++c) {
+        v[c] = (mags[c] * s16) * scale2;  // exact product, one rounding
+        // a magnitude above the block max (|q0| > 128) occurs in no element of
+        // this half: its table entry is never read, so it is kept off the tie check
+        const float q0 = fminf(fmaxf(v[c] * r, -128.0f), 128.0f);
+        const float tt = rintf(q0);
+        is_half[c] = use_half && fabsf(v[c]) == half_amax;
+        near[c] = !is_half[c] && fabsf(q0 - tt) > kTieGuard;
+        t[c] = is_half[c] ? q_half_signed : tt;
+        any_near |= near[c];
     }
-    return (int)t;
+    if (sub || (!exact_r && any_near)) {
+#pragma unroll
+        for (int c = 1; c < 8; ++c) {
+            if (sub)
+                t[c] = fminf(fmaxf(rintf(v[c] / s), -127.0f), 127.0f);
+            else if (near[c])
+                t[c] = rintf(v[c] / s);
+        }
+    }
+    qm[0] = 0;
+#pragma unroll
+    for (int c = 1; c < 8; ++c) qm[c] = (int)t[c];
 }
 
 // Quantize one 32-element block: 16 packed bytes and its two E4M3 scales.
@@ -500,15 +539,13 @@ __device__ __forceinline__ void requant_w_block(uint4 p, uint32_t sc, float scal
         const bool sub = s < 0x1p-126f;
         const bool pow2 = (sb & 0x007FFFFFu) == 0;
         const float r = pow2 ? __uint_as_float(0x7F000000u - (sb & 0x7F800000u)) : __builtin_amdgcn_rcpf(s);
-        const float mags[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+        const bool use_half = s >= 0x1p-100f;
+        const float q_half = fmaf(-127.0f, s, amax) < -0x1p-18f * s ? 63.0f : 64.0f;
         uint32_t tab[2][4];  // pos_lo, pos_hi, neg_lo, neg_hi per half
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             int qm[8];
-            qm[0] = 0;
-#pragma unroll
-            for (int c = 1; c < 8; ++c)
-                qm[c] = w_code((mags[c] * s16[h]) * scale2, s, r, pow2, sub);  // exact product, one rounding
+            half_codes(s16[h], scale2, amax, s, r, pow2, sub, use_half, q_half, qm);
             tab[h][0] = pack4_i8(qm[0], qm[1], qm[2], qm[3]);
             tab[h][1] = pack4_i8(qm[4], qm[5], qm[6], qm[7]);
             tab[h][2] = pack4_i8(-qm[0], -qm[1], -qm[2], -qm[3]);

@@ -109,8 +109,10 @@ def test_requant_a_zero_and_special_blocks():
 
 
 @pytest.mark.parametrize("scale2", [np.float32(1 / 64), inputs.SCALE2_1_448, np.float32(0.0123456),
-                                    np.float32(-3.0e-3), np.float32(1e-38)])
+                                    np.float32(-3.0e-3), np.float32(1e-38), np.float32(2.0 ** -92)])
 def test_requant_w_exhaustive_scale_pairs(scale2):
+    # (scale2 = 2^-92 puts the block scales of the sweep on both sides of 2^-100,
+    # where the kernel stops using its closed form for half-max elements)
     # Every pair of finite positive E4M3 codes (sa, sb) on the two halves, each half
     # holding all 16 E2M1 codes; plus negative scale codes.
     codes = [c for c in range(0x01, 0x7F)]
@@ -131,6 +133,24 @@ def test_requant_w_exhaustive_scale_pairs(scale2):
     q_ref, s_ref = oracle.requant_w(packed, pairs, scale2)
     q, s = gpu_requant_w(packed, pairs, scale2)
     _assert_same(f"pairs {float(scale2)}", host(q), host(s), q_ref, s_ref)
+
+
+@pytest.mark.parametrize("scale2", [np.float32(0.0123456), np.float32(1 / 64), np.float32(2.0 ** -92),
+                                    np.float32(-3.0e-3)])
+def test_requant_w_half_of_block_max(scale2):
+    # Magnitudes 6 and +-3 under one scale on both halves: the 3s are exactly half the
+    # block max, so their quotient is 63.5 moved by the rounding of s, and the code is
+    # 63 or 64 depending on that rounding.  Over the normal E4M3 scale codes both occur.
+    codes = np.arange(0x08, 0x7F, dtype=np.uint8)
+    e4m3 = np.repeat(codes[:, None], 2, axis=1)
+    half = np.array([0x57, 0xD5, 0, 0, 0, 0, 0, 0], np.uint8)   # +6 +3 | +3 -3 | zeros
+    packed = np.tile(np.concatenate([half, half]), (codes.shape[0], 1))
+    q_ref, s_ref = oracle.requant_w(packed, e4m3, scale2)
+    halves = np.abs(q_ref[:, [1, 2, 3, 17, 18, 19]].astype(np.int32))
+    if scale2 != np.float32(-3.0e-3):
+        assert set(np.unique(halves)) == {63, 64}
+    q, s = gpu_requant_w(packed, e4m3, scale2)
+    _assert_same(f"half of max {float(scale2)}", host(q), host(s), q_ref, s_ref)
 
 
 def test_requant_w_random_codes_and_sparse_blocks():
