@@ -18,7 +18,7 @@ constexpr int kRqaUnroll = 2;        // chunks per lane, loads issued together
 // 32 int8 out), 256 lanes per workgroup.
 constexpr int kRqwThreads = 256;
 constexpr int kRqwUnroll = 2;        // blocks per lane, loads issued together
-constexpr int kSiluUnroll = 2;       // chunks per lane and pass of the SiLU table kernel
+constexpr int kSiluMinPasses = 8;    // fewest passes per workgroup for the SiLU table kernel
 constexpr int kSiluThreads = 512;    // lanes per workgroup of the SiLU table kernel
 
 // ---- GEMM (m > 16) --------------------------------------------------------

@@ -290,54 +290,59 @@ __global__ __launch_bounds__(kRqaThreads) void silu_requant_kernel(const uint16_
 }
 
 // Table kernel (large inputs): persistent workgroups each fill the SiLU table
-// in LDS once, then stride over groups of kSiluThreads * U chunks.  Each lane
-// tracks the (row, column) of its chunks incrementally instead of dividing.
-template <int U>
+// in LDS once, then stride over the chunks, one per lane and pass.  The loads
+// run two passes ahead of the arithmetic (three register sets, the loop
+// unrolled by three so each set keeps its registers): the first two passes'
+// loads go out before the table fill, and every pass issues the loads of the
+// pass after next before computing its own.  Each lane tracks the (row, column)
+// of its next load incrementally instead of dividing.
 __global__ __launch_bounds__(kSiluThreads) void silu_requant_table_kernel(
     const uint16_t *__restrict__ gate, const uint16_t *__restrict__ up, uint32_t ld,
     uint2 *__restrict__ q, float *__restrict__ scale, uint64_t nchunks, uint32_t kc) {
     __shared__ float tab[kSiluTable];
-    for (int i = threadIdx.x; i < kSiluTable; i += kSiluThreads)
-        tab[i] = silu32(__uint_as_float(silu_table_bits(i) << 16));
-    __syncthreads();
-    const uint64_t stride = (uint64_t)gridDim.x * kSiluThreads * U;
+    const uint64_t stride = (uint64_t)gridDim.x * kSiluThreads;
     const uint64_t s_row = stride / kc;
     const uint32_t s_col = (uint32_t)(stride % kc);
     const uint64_t last = silu_chunk_offset(nchunks - 1, kc, ld);
-    uint64_t row[U];
-    uint32_t col[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const uint64_t c = (uint64_t)blockIdx.x * kSiluThreads * U + u * kSiluThreads + threadIdx.x;
-        row[u] = c / kc;
-        col[u] = (uint32_t)(c % kc);
-    }
-    for (uint64_t g0 = (uint64_t)blockIdx.x * kSiluThreads * U; g0 < nchunks; g0 += stride) {
-        uint4 gr[U], ur[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint64_t c = g0 + u * kSiluThreads + threadIdx.x;
-            const uint64_t off = c < nchunks ? row[u] * ld + col[u] * 8 : last;
-            gr[u] = *reinterpret_cast<const uint4 *>(gate + off);
-            ur[u] = *reinterpret_cast<const uint4 *>(up + off);
+    const uint64_t c0 = (uint64_t)blockIdx.x * kSiluThreads + threadIdx.x;
+    uint64_t cl = c0, row = c0 / kc;  // chunk, row and column of the next load
+    uint32_t col = (uint32_t)(c0 % kc);
+    auto load = [&](uint4 &g, uint4 &u) {
+        const uint64_t off = cl < nchunks ? row * ld + col * 8 : last;
+        g = *reinterpret_cast<const uint4 *>(gate + off);
+        u = *reinterpret_cast<const uint4 *>(up + off);
+        cl += stride;
+        col += s_col;
+        row += s_row;
+        if (col >= kc) {
+            col -= kc;
+            ++row;
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint64_t c = g0 + u * kSiluThreads + threadIdx.x;
-            float h[8], s;
-            silu_mul_chunk(gr[u], ur[u], tab, h);
-            const uint2 packed = requant_a_vals(h, s);
-            if (c < nchunks) {
-                q[c] = packed;
-                if ((c & 3) == 0) scale[c >> 2] = s;
-            }
-            col[u] += s_col;
-            row[u] += s_row;
-            if (col[u] >= kc) {
-                col[u] -= kc;
-                ++row[u];
-            }
-        }
+    };
+    uint4 g0, u0, g1, u1, g2, u2;
+    load(g0, u0);
+    load(g1, u1);
+    for (int i = threadIdx.x; i < kSiluTable; i += kSiluThreads)
+        tab[i] = silu32(__uint_as_float(silu_table_bits(i) << 16));
+    __syncthreads();
+    uint64_t c = c0;  // chunk of the next computation
+    auto compute = [&](const uint4 &g, const uint4 &u) {
+        float h[8], s;
+        silu_mul_chunk(g, u, tab, h);
+        const uint2 packed = requant_a_vals(h, s);
+        q[c] = packed;
+        if ((c & 3) == 0) scale[c >> 2] = s;
+        c += stride;
+    };
+    while (c < nchunks) {
+        load(g2, u2);
+        compute(g0, u0);
+        if (c >= nchunks) break;
+        load(g0, u0);
+        compute(g1, u1);
+        if (c >= nchunks) break;
+        load(g1, u1);
+        compute(g2, u2);
     }
 }
 
@@ -609,12 +614,11 @@ hipError_t launch_silu_requant(const uint16_t *gate, const uint16_t *up, uint32_
     const uint32_t kc = k / 8;
     const uint64_t nchunks = (uint64_t)m * kc;
     // Table kernel once there is work for at least one workgroup per CU with
-    // 4 passes each (its table costs ~16 SiLU evaluations per lane); up to 4
-    // workgroups of 8 waves per CU (LDS: 31 KB each).
-    const uint64_t per_wg = (uint64_t)kSiluThreads * kSiluUnroll;
-    const uint64_t table_grid = min(div_up(nchunks, per_wg * 4), (uint64_t)4 * kGemmCus);
+    // kSiluMinPasses passes each (its table costs ~16 SiLU evaluations per
+    // lane); up to 4 workgroups of 8 waves per CU (LDS: 32 KB each).
+    const uint64_t table_grid = min(div_up(nchunks, (uint64_t)kSiluThreads * kSiluMinPasses), (uint64_t)4 * kGemmCus);
     if (table_grid >= (uint64_t)kGemmCus) {
-        hipLaunchKernelGGL(silu_requant_table_kernel<kSiluUnroll>, dim3((uint32_t)table_grid), dim3(kSiluThreads),
+        hipLaunchKernelGGL(silu_requant_table_kernel, dim3((uint32_t)table_grid), dim3(kSiluThreads),
                            0, s, gate, up, ld, reinterpret_cast<uint2 *>(a_i8), a_scale, nchunks, kc);
     } else {
         const uint64_t grid = div_up(nchunks, (uint64_t)kRqaThreads * kRqaUnroll);

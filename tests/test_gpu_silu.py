@@ -19,9 +19,11 @@ def _same(name, q, s, q_ref, s_ref):
     assert bad_q == 0 and bad_s == 0
 
 
-# 128 x 512 runs the per-element kernel; 1024 x 4096 (4.2 M elements) the
-# LDS-table kernel, whose closed-form ranges and every table entry are hit.
-@pytest.mark.parametrize("m,k", [(128, 512), (1024, 4096)])
+# 128 x 512 runs the per-element kernel.  The LDS-table kernel takes inputs with
+# at least 256 x 4096 chunks of 8 elements: 2049 x 4160 (1 065 480 chunks, 261
+# persistent workgroups, a ragged last pass) runs it, with its closed-form
+# ranges and every table entry hit.
+@pytest.mark.parametrize("m,k", [(128, 512), (2049, 4160)])
 def test_every_finite_bf16_gate(m, k):
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     bits = bits[((bits >> 7) & 0xFF) != 0xFF]
@@ -55,7 +57,7 @@ def test_workload_full():
     _same("ffn_down_input", host(q), host(s), q_ref, s_ref)
 
 
-@pytest.mark.parametrize("m,k", [(37, 640), (512, 8192)])
+@pytest.mark.parametrize("m,k", [(37, 640), (512, 8192), (1100, 8192)])   # the last on the table kernel
 def test_halves_of_one_buffer(m, k):
     # gate and up as the two halves of one [m, 2k] gate+up output (row pitch 2k)
     rng = np.random.default_rng(9)
