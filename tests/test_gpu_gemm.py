@@ -53,6 +53,27 @@ def test_gemm_parity_random(m, n, k):
     _check(f"gemm {m}x{n}x{k}", host(out), y, t, k)
 
 
+def test_gemm_big_tiles_ragged():
+    # m > 128 with at least 512 tiles of 128 x 128 takes the big-tile kernel; here the
+    # last tile row (1024..1099), the last tile column (7296..7399) and the last K stage
+    # (33 blocks: 8 stages of 4 and one of 1) are all partial.  Rows are independent,
+    # so sampled rows (both sides of each tile edge) are checked whole against the
+    # oracle, and guard bands around the output catch stores past its end.
+    m, n, k = 1100, 7400, 1056
+    assert m > 128 and -(-m // 128) * -(-n // 128) >= 512
+    a, w, a_s, w_s = _rand_operands(4242, m, n, k, zero_frac=0.02)
+    pad = 4096
+    buf = torch.full((pad + m * n + pad,), 0x7B7B, dtype=torch.int16, device=DEV)
+    out = buf[pad:pad + m * n].view(m, n)
+    bsr.int8_gemm_blockscaled_ex(to_dev(a), to_dev(w), to_dev(a_s), to_dev(w_s), out, path=bsr.PATH_GEMM)
+    hb = host(buf)
+    assert np.all(hb[:pad] == 0x7B7B) and np.all(hb[pad + m * n:] == 0x7B7B)
+    rows = np.array([0, 1, 127, 128, 555, 1023, 1024, 1050, 1098, 1099])
+    y, t = oracle.gemm_ref(a[rows], w, a_s[rows], w_s)
+    _check(f"gemm big tiles {m}x{n}x{k}, rows {rows.tolist()}",
+           hb[pad:pad + m * n].reshape(m, n)[rows], y, t, k)
+
+
 # K = 1056 (33 blocks) and 2400 (75): direct kernel with per-element scale
 # loads; 2176 (68 blocks, scale rows padded to 128 in LDS) and 4096: staged
 # kernel; m = 8 at K = 16384 needs 180 KB of LDS, so the direct kernel with
