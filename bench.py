@@ -183,7 +183,9 @@ def main():
                                              frac_hbm=bytes_w / b_w / 1e9 / PEAK_HBM_GBS),
                 "requant_a_int8": dict(us_burst=b_a * 1e6, gbs=bytes_a / b_a / 1e9,
                                        frac_hbm=bytes_a / b_a / 1e9 / PEAK_HBM_GBS),
-                "int8_gemm_blockscaled": dict(us_in_step_mean=t_g.mean() * 1e6, us_in_step_min=t_g.min() * 1e6,
+                "int8_gemm_blockscaled": dict(us_in_step_mean=t_g.mean() * 1e6,
+                                              us_in_step_median=float(np.median(t_g)) * 1e6,
+                                              us_in_step_min=t_g.min() * 1e6,
                                               us_burst=b_g * 1e6, tops=gemm_tops,
                                               frac_int8=gemm_tops / PEAK_INT8_TOPS),
                 "requant_a_plus_gemm": dict(us_burst=b_ag * 1e6, tops=ops / b_ag / 1e12),
@@ -340,6 +342,27 @@ def main():
         torch.cuda.empty_cache()
         rec["layouts"] = lay
 
+    # ------------------------------------------------------------ context
+    # achievable streaming bandwidth: a plain device copy (torch's), read + write
+    # counted, 512 MiB each way, ten copies between one event pair
+    if args.only in ("all", "prefill"):
+        src = torch.ones(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_c = e0.elapsed_time(e1) * 1e-3 / 10
+        rec["copy_context"] = dict(bytes_per_copy=2 * src.numel(), us=t_c * 1e6,
+                                   gbs=2 * src.numel() / t_c / 1e9,
+                                   frac_hbm=2 * src.numel() / t_c / 1e9 / PEAK_HBM_GBS)
+        del src, dst
+        torch.cuda.empty_cache()
+
     # ------------------------------------------------------------ CPU oracle
     cpu = None
     if not args.no_cpu_baseline and args.only in ("all", "prefill"):
@@ -410,6 +433,8 @@ def main():
         line["silu_mul_requant"] = rec["silu"]
     if "layouts" in rec:
         line["activation_layouts"] = rec["layouts"]
+    if "copy_context" in rec:
+        line["copy_context"] = rec["copy_context"]
     print(json.dumps(line), flush=True)
 
 
