@@ -388,6 +388,26 @@ def main():
                            f"GEMM reference on {rows_done} of {M} rows ({t_rows:.2f} s) "
                            f"extrapolated linearly to all rows"),
                    seconds_extrapolated=t_full)
+        # the same oracle on one thread: 256 weight rows, 64 activation rows and 16
+        # GEMM rows, each extrapolated linearly to the whole workload
+        oracle.set_threads(1)
+        try:
+            t0 = time.perf_counter()
+            oracle.requant_w(packed[:256], e4m3[:256], proj.scale2)
+            t1_w = (time.perf_counter() - t0) * N / 256
+            t0 = time.perf_counter()
+            oracle.requant_a(a_bits[:64])
+            t1_a = (time.perf_counter() - t0) * M / 64
+            t0 = time.perf_counter()
+            oracle.gemm_ref(oa[:16], ow, osa[:16], osw)
+            t1_g = (time.perf_counter() - t0) * M / 16
+        finally:
+            oracle.set_threads(cores)
+        t1 = t1_w + t1_a + t1_g
+        cpu["single_thread"] = dict(value=2.0 * M * N * K / t1 / 1e12, unit="TOPS", cores=1,
+                                    sample="weight requant on 256 of N rows, activation requant on 64 of M "
+                                           "rows, GEMM reference on 16 of M rows, each extrapolated linearly",
+                                    seconds_extrapolated=t1)
 
     pre = rec.get("prefill")
     line = {
