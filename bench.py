@@ -9,18 +9,22 @@ reported under "decode" in GB/s of algorithmic HBM traffic.
 
 Inputs are resident in HBM before timing.  Every timed iteration uses a
 different set of buffers (rotating through enough sets that each set has left
-the 256 MB Infinity Cache before it is used again).  The step time is the
-wall clock of the timed steps between two device synchronizations; inside
-the timed region only the GEMM launches are bracketed by HIP events (on the
-stream the launches use), which gives the roofline's kernel duration.  Each
-kernel is also timed alone, back to back over rotating buffers with one event
-pair around the whole burst ("us_burst"), which leaves out the per-launch
-event overhead that in-step brackets carry.  The CPU oracle is timed beside it
-on a bounded sample (rank 0, one GPU only).
+the 256 MB Infinity Cache before it is used again).  Before the warm-up steps
+the step runs untimed for ~100 ms (and every burst below for ~50 ms), so the
+GPU's clocks have reached their steady state.  The step time is the wall
+clock of the timed steps between two device synchronizations; inside the
+timed region only the GEMM launches are bracketed by HIP events (timing-only
+events without the system-scope fence, on the stream the launches use), which
+gives the roofline's kernel duration.  Each kernel is also timed alone, back
+to back over rotating buffers with one event pair around the whole burst
+("us_burst"), which leaves out the per-launch event overhead that in-step
+brackets carry.  The CPU oracle is timed beside it on a bounded sample (rank
+0, one GPU only).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -71,6 +75,63 @@ def _traffic(kernel, source_files, launches_bytes_alg):
     if not rec or rec.get("source_digest") != _source_digest(source_files):
         return None
     return rec.get("bytes_per_launch")
+
+
+class HipEvent:
+    """A HIP event for timing only, recorded on a given stream: created with
+    hipEventDisableSystemFence, so recording it skips the system-scope cache
+    writeback and invalidation that a default event (torch's) performs, which
+    would otherwise stall the stream between the kernels it brackets."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def _runtime(cls):
+        if cls._hip is None:
+            # the HIP runtime torch loaded (the one that owns its streams)
+            with open("/proc/self/maps") as f:
+                paths = [ln.split()[-1] for ln in f if "libamdhip64.so" in ln]
+            cls._hip = ctypes.CDLL(paths[0] if paths else "libamdhip64.so")
+        return cls._hip
+
+    def __init__(self):
+        self.h = ctypes.c_void_p()
+        rc = self._runtime().hipEventCreateWithFlags(ctypes.byref(self.h), ctypes.c_uint(self.DISABLE_SYSTEM_FENCE))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags: {rc}")
+
+    def record(self, stream):
+        rc = self._runtime().hipEventRecord(self.h, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord: {rc}")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both complete: synchronize first)."""
+        ms = ctypes.c_float()
+        rc = self._runtime().hipEventElapsedTime(ctypes.byref(ms), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime: {rc}")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.h:
+            self._hip.hipEventDestroy(self.h)
+
+
+def settle(fn, seconds):
+    """Run fn(0), fn(1), ... untimed for about `seconds` of wall time.  Under a
+    sustained load the GPU's clocks take ~35 ms to reach their steady state
+    (the prefill step falls from ~137 to ~112 us over that time), so every
+    timed region is preceded by this."""
+    import torch
+    t0, i = time.perf_counter(), 0
+    while True:
+        for _ in range(16):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
 
 
 def main():
@@ -133,11 +194,10 @@ def main():
             ev[1].record(stream)
 
     def burst(fn, reps):
-        """Average duration of `reps` back-to-back launches fn(i) (one event pair)."""
-        for i in range(3):
-            fn(i)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        """Average duration of `reps` back-to-back launches fn(i) (one event pair),
+        after ~50 ms of the same launches untimed."""
+        settle(fn, 0.05)
+        e0, e1 = HipEvent(), HipEvent()
         e0.record(stream)
         for i in range(reps):
             fn(i)
@@ -146,9 +206,10 @@ def main():
         return e0.elapsed_time(e1) * 1e-3 / reps
 
     if args.only in ("all", "prefill"):
+        settle(lambda i: step(sets[i % nsets]), 0.1)
         for i in range(args.warmup):
             step(sets[i % nsets])
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        evs = [[HipEvent(), HipEvent()] for _ in range(args.steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
@@ -221,27 +282,14 @@ def main():
             a_s = torch.empty((p.m, p.k // 32), dtype=torch.float32, device=dev)
             out = torch.empty((p.m, p.n), dtype=torch.int16, device=dev)
             bsr.requant_a_int8(a_dev, a_i8, a_s)
-            for i in range(10):
-                wi, ws = copies[i % ncopy]
-                bsr.int8_gemm_blockscaled(a_i8, wi, a_s, ws, out)
-            torch.cuda.synchronize()
             it = args.decode_iters
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(it):
-                wi, ws = copies[i % ncopy]
-                bsr.int8_gemm_blockscaled(a_i8, wi, a_s, ws, out, stream=stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            t_v = e0.elapsed_time(e1) * 1e-3 / it
-            e0.record(stream)
-            for i in range(it):
-                wi, ws = copies[i % ncopy]
+            t_v = burst(lambda i: bsr.int8_gemm_blockscaled(a_i8, copies[i % ncopy][0], a_s, copies[i % ncopy][1],
+                                                            out, stream=stream), it)
+
+            def requant_and_gemv(i):
                 bsr.requant_a_int8(a_dev, a_i8, a_s, stream=stream)
-                bsr.int8_gemm_blockscaled(a_i8, wi, a_s, ws, out, stream=stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            t_qv = e0.elapsed_time(e1) * 1e-3 / it
+                bsr.int8_gemm_blockscaled(a_i8, copies[i % ncopy][0], a_s, copies[i % ncopy][1], out, stream=stream)
+            t_qv = burst(requant_and_gemv, it)
             # the path-invariant GEMV (one FP32 chain per output, in the GEMM's order)
             t_inv = burst(lambda i: bsr.int8_gemm_blockscaled_ex(a_i8, copies[i % ncopy][0], a_s, copies[i % ncopy][1],
                                                                  out, path=bsr.PATH_INVARIANT, stream=stream), it)
@@ -350,7 +398,8 @@ def main():
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        settle(lambda i: dst.copy_(src), 0.05)
+        e0, e1 = HipEvent(), HipEvent()
         e0.record(stream)
         for _ in range(10):
             dst.copy_(src)
