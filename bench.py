@@ -114,8 +114,11 @@ class HipEvent:
         return ms.value
 
     def __del__(self):
-        if self._hip is not None and self.h:
-            self._hip.hipEventDestroy(self.h)
+        try:
+            if self._hip is not None and self.h:
+                self._hip.hipEventDestroy(self.h)
+        except Exception:  # interpreter shutdown: the runtime may already be gone
+            pass
 
 
 def settle(fn, seconds):
