@@ -20,10 +20,11 @@ def _same(name, q, s, q_ref, s_ref):
 
 
 # 128 x 512 runs the per-element kernel.  The LDS-table kernel takes inputs with
-# at least 256 x 4096 chunks of 8 elements: 2049 x 4160 (1 065 480 chunks, 261
-# persistent workgroups, a ragged last pass) runs it, with its closed-form
-# ranges and every table entry hit.
-@pytest.mark.parametrize("m,k", [(128, 512), (2049, 4160)])
+# at least 256 x 4096 chunks of 8 elements: 2048 x 4096 is exactly that (256
+# persistent workgroups, 8 whole passes), 2049 x 4160 (1 065 480 chunks, 261
+# workgroups) ends in a ragged pass; both hit the closed-form ranges and every
+# table entry.
+@pytest.mark.parametrize("m,k", [(128, 512), (2048, 4096), (2049, 4160)])
 def test_every_finite_bf16_gate(m, k):
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     bits = bits[((bits >> 7) & 0xFF) != 0xFF]
