@@ -307,7 +307,21 @@ def main():
             t_4 = burst(lambda i: bsr.w4a16_gemv(a_dev, copies4[i % ncopy4][0], copies4[i % ncopy4][1],
                                                  float(p.scale2), out4, stream=stream), it)
             alg4 = w4bytes + p.m * p.k * 2 + 2 * p.m * p.n
-            dec[p.name] = dict(m=p.m, n=p.n, k=p.k, gemv_us_burst=t_v * 1e6,
+            cpu_dec = {}
+            if not args.no_cpu_baseline:
+                # the oracle beside it (host threads): activation requant + GEMV reference on
+                # the weight requantized once beforehand, and the W4A16 reference
+                ow, osw = oracle.requant_w(wp, we, p.scale2)
+                t0 = time.perf_counter()
+                oa, osa = oracle.requant_a(a)
+                oracle.gemm_ref(oa, ow, osa, osw)
+                t_o = time.perf_counter() - t0
+                t0 = time.perf_counter()
+                oracle.w4a16_ref(a, wp, we, p.scale2)
+                t_o4 = time.perf_counter() - t0
+                cpu_dec = dict(cpu_oracle_requant_a_plus_gemv_us=t_o * 1e6, cpu_oracle_w4a16_us=t_o4 * 1e6,
+                               cpu_cores=oracle.max_threads())
+            dec[p.name] = dict(m=p.m, n=p.n, k=p.k, gemv_us_burst=t_v * 1e6, **cpu_dec,
                                gemv_gbs=alg / t_v / 1e9, gemv_frac_hbm=alg / t_v / 1e9 / PEAK_HBM_GBS,
                                requant_a_plus_gemv_us_burst=t_qv * 1e6,
                                invariant_gemv_us_burst=t_inv * 1e6,
@@ -336,6 +350,11 @@ def main():
         rec["silu"] = dict(workload=f"SiLU(gate) * up -> int8 per 32, M={src.m} I={src.k}",
                            us_burst=t_s * 1e6, gbs=sbytes / t_s / 1e9,
                            frac_hbm=sbytes / t_s / 1e9 / PEAK_HBM_GBS)
+        if not args.no_cpu_baseline:
+            t0 = time.perf_counter()
+            oracle.silu_mul_requant(g_bits, u_bits)
+            rec["silu"]["cpu_oracle_us"] = (time.perf_counter() - t0) * 1e6
+            rec["silu"]["cpu_cores"] = oracle.max_threads()
         del ssets
         torch.cuda.empty_cache()
 
