@@ -457,9 +457,10 @@ hipError_t launch_w4a16_stream(const uint16_t *x, const uint8_t *w_packed, const
     const uint32_t tiles = (uint32_t)div_up(n, kGemvCols);
     const uint32_t nchunks = k / kW4ChunkK;
     // as many waves (2 to 8) as let the workgroups a CU must run share its LDS
-    // at once (measured: N = 14336 wants 8 waves at m <= 2 but 2 at m = 8)
+    // at once, except that m <= 2 always takes 8 (N = 14336, K = 4096: 9.6-9.7 us
+    // against 9.9 with the 6 that fit four workgroups per CU; m = 8 wants 2)
     const uint32_t wg_per_cu = (uint32_t)div_up(tiles, kGemmCus);
-    uint32_t waves = max(2u, (160u * 1024u / wg_per_cu) / ring_bytes);
+    uint32_t waves = ROWS <= 2 ? max_waves : max(2u, (160u * 1024u / wg_per_cu) / ring_bytes);
     waves = min(min(waves, max_waves), nchunks);
     const uint32_t cpw = (uint32_t)div_up(nchunks, waves);
     waves = (uint32_t)div_up(nchunks, cpw);
