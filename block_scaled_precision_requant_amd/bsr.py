@@ -62,7 +62,12 @@ def status_string(status: int) -> str:
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+    # runs after every argument's shape and element checks
+    if t is None:
+        return ctypes.c_void_p(0)
+    if not t.is_cuda:
+        raise ValueError("arguments must be device tensors")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(stream, like):
@@ -71,13 +76,25 @@ def _stream(stream, like):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _shape(t, shape, what):
+# Element kinds the kernels read and write: byte codes (int8, packed E2M1,
+# E4M3), 16-bit BF16 bits (any 2-byte dtype: torch.bfloat16, int16, uint16)
+# and binary32 scales.
+BYTES, BF16, F32 = "1-byte", "2-byte", "float32"
+
+
+def _shape(t, shape, what, kind):
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{what}: must be contiguous")
-    if not t.is_cuda:
-        raise ValueError(f"{what}: must be a device tensor")
+    _kind(t, what, kind)
+
+
+def _kind(t, what, kind):
+    ok = (t.dtype == torch.float32 if kind == F32 else
+          t.element_size() == (1 if kind == BYTES else 2) and not t.dtype.is_complex)
+    if not ok:
+        raise ValueError(f"{what}: dtype {t.dtype}, expected {kind} elements")
 
 
 def _done(status, what):
@@ -90,10 +107,10 @@ def requant_w_nvfp4_int8(w_packed, w_e4m3, scale2, w_i8, w_scale, stream=None):
     w_i8 [N,K] int8 and w_scale [N,K/32] float32 (both preallocated)."""
     n, half_k = w_packed.shape
     k = 2 * half_k
-    _shape(w_packed, (n, k // 2), "w_packed")
-    _shape(w_e4m3, (n, k // 16), "w_e4m3")
-    _shape(w_i8, (n, k), "w_i8")
-    _shape(w_scale, (n, k // 32), "w_scale")
+    _shape(w_packed, (n, k // 2), "w_packed", BYTES)
+    _shape(w_e4m3, (n, k // 16), "w_e4m3", BYTES)
+    _shape(w_i8, (n, k), "w_i8", BYTES)
+    _shape(w_scale, (n, k // 32), "w_scale", F32)
     st = lib().requant_w_nvfp4_int8(_ptr(w_packed), _ptr(w_e4m3), float(scale2), _ptr(w_i8),
                                     _ptr(w_scale), n, k, _stream(stream, w_i8))
     _done(st, "requant_w_nvfp4_int8")
@@ -102,9 +119,9 @@ def requant_w_nvfp4_int8(w_packed, w_e4m3, scale2, w_i8, w_scale, stream=None):
 def requant_a_int8(a_bf16, a_i8, a_scale, stream=None):
     """BF16 activations a_bf16 [M,K] -> a_i8 [M,K] int8 and a_scale [M,K/32] float32."""
     m, k = a_bf16.shape
-    _shape(a_bf16, (m, k), "a_bf16")
-    _shape(a_i8, (m, k), "a_i8")
-    _shape(a_scale, (m, k // 32), "a_scale")
+    _shape(a_bf16, (m, k), "a_bf16", BF16)
+    _shape(a_i8, (m, k), "a_i8", BYTES)
+    _shape(a_scale, (m, k // 32), "a_scale", F32)
     st = lib().requant_a_int8(_ptr(a_bf16), _ptr(a_i8), _ptr(a_scale), m, k, _stream(stream, a_i8))
     _done(st, "requant_a_int8")
 
@@ -118,13 +135,12 @@ def silu_mul_requant_int8(gate, up, a_i8, a_scale, stream=None):
     if tuple(up.shape) != (m, k):
         raise ValueError(f"up: shape {tuple(up.shape)}, expected {(m, k)}")
     for t, what in ((gate, "gate"), (up, "up")):
-        if not t.is_cuda:
-            raise ValueError(f"{what}: must be a device tensor")
-        if t.element_size() != 2 or (m > 1 and t.stride(1) != 1) or (m > 1 and t.stride(0) != gate.stride(0)):
+        _kind(t, what, BF16)
+        if (m > 1 and t.stride(1) != 1) or (m > 1 and t.stride(0) != gate.stride(0)):
             raise ValueError(f"{what}: 16-bit rows with unit column stride and the gate's row stride")
     ld = gate.stride(0) if m > 1 else k
-    _shape(a_i8, (m, k), "a_i8")
-    _shape(a_scale, (m, k // 32), "a_scale")
+    _shape(a_i8, (m, k), "a_i8", BYTES)
+    _shape(a_scale, (m, k // 32), "a_scale", F32)
     st = lib().silu_mul_requant_int8(_ptr(gate), _ptr(up), ld, _ptr(a_i8), _ptr(a_scale), m, k,
                                      _stream(stream, a_i8))
     _done(st, "silu_mul_requant_int8")
@@ -135,10 +151,10 @@ def w4a16_gemv(x_bf16, w_packed, w_e4m3, scale2, out, stream=None):
     w_e4m3 [N,K/16] u8, scale2), dequantized on the fly."""
     m, k = x_bf16.shape
     n = w_packed.shape[0]
-    _shape(x_bf16, (m, k), "x_bf16")
-    _shape(w_packed, (n, k // 2), "w_packed")
-    _shape(w_e4m3, (n, k // 16), "w_e4m3")
-    _shape(out, (m, n), "out")
+    _shape(x_bf16, (m, k), "x_bf16", BF16)
+    _shape(w_packed, (n, k // 2), "w_packed", BYTES)
+    _shape(w_e4m3, (n, k // 16), "w_e4m3", BYTES)
+    _shape(out, (m, n), "out", BF16)
     st = lib().w4a16_gemv(_ptr(x_bf16), _ptr(w_packed), _ptr(w_e4m3), float(scale2), _ptr(out), m, n, k,
                           _stream(stream, out))
     _done(st, "w4a16_gemv")
@@ -148,11 +164,11 @@ def int8_gemm_blockscaled_ex(a_i8, w_i8, a_scale, w_scale, out, path=PATH_AUTO, 
     """out [M,N] BF16 = block-scaled int8 GEMM of a_i8 [M,K] and w_i8 [N,K]."""
     m, k = a_i8.shape
     n = w_i8.shape[0]
-    _shape(a_i8, (m, k), "a_i8")
-    _shape(w_i8, (n, k), "w_i8")
-    _shape(a_scale, (m, k // 32), "a_scale")
-    _shape(w_scale, (n, k // 32), "w_scale")
-    _shape(out, (m, n), "out")
+    _shape(a_i8, (m, k), "a_i8", BYTES)
+    _shape(w_i8, (n, k), "w_i8", BYTES)
+    _shape(a_scale, (m, k // 32), "a_scale", F32)
+    _shape(w_scale, (n, k // 32), "w_scale", F32)
+    _shape(out, (m, n), "out", BF16)
     st = lib().int8_gemm_blockscaled_ex(_ptr(a_i8), _ptr(w_i8), _ptr(a_scale), _ptr(w_scale), _ptr(out),
                                         m, n, k, _stream(stream, out), int(path))
     _done(st, "int8_gemm_blockscaled_ex")
@@ -163,11 +179,11 @@ def int8_gemm_blockscaled(a_i8, w_i8, a_scale, w_scale, out, stream=None):
     M <= 48 when K % 256 == 0 and N <= 4096; else the GEMM)."""
     m, k = a_i8.shape
     n = w_i8.shape[0]
-    _shape(a_i8, (m, k), "a_i8")
-    _shape(w_i8, (n, k), "w_i8")
-    _shape(a_scale, (m, k // 32), "a_scale")
-    _shape(w_scale, (n, k // 32), "w_scale")
-    _shape(out, (m, n), "out")
+    _shape(a_i8, (m, k), "a_i8", BYTES)
+    _shape(w_i8, (n, k), "w_i8", BYTES)
+    _shape(a_scale, (m, k // 32), "a_scale", F32)
+    _shape(w_scale, (n, k // 32), "w_scale", F32)
+    _shape(out, (m, n), "out", BF16)
     st = lib().int8_gemm_blockscaled(_ptr(a_i8), _ptr(w_i8), _ptr(a_scale), _ptr(w_scale), _ptr(out),
                                      m, n, k, _stream(stream, out))
     _done(st, "int8_gemm_blockscaled")
@@ -184,9 +200,9 @@ def quantize_act(a_bf16, q, scale, group=32, fmt=FMT_INT8, stream=None):
     """BF16 a_bf16 [M,K] -> codes q [M,K] (uint8: int8 or E4M3 bits) and float32
     scales [M, K/group] (group 32 or 128) or [M, 1] (group 0: one per row)."""
     m, k = a_bf16.shape
-    _shape(a_bf16, (m, k), "a_bf16")
-    _shape(q, (m, k), "q")
-    _shape(scale, (m, _scale_cols(k, group)), "scale")
+    _shape(a_bf16, (m, k), "a_bf16", BF16)
+    _shape(q, (m, k), "q", BYTES)
+    _shape(scale, (m, _scale_cols(k, group)), "scale", F32)
     st = lib().quantize_act(_ptr(a_bf16), _ptr(q), _ptr(scale), m, k, int(group), int(fmt), _stream(stream, q))
     _done(st, "quantize_act")
 
@@ -196,11 +212,11 @@ def int8_gemm_blockscaled_agroup(a_i8, w_i8, a_scale, a_group, w_scale, out, pat
     (a_group 32 or 128) or [M, 1] (a_group 0: one per row)."""
     m, k = a_i8.shape
     n = w_i8.shape[0]
-    _shape(a_i8, (m, k), "a_i8")
-    _shape(w_i8, (n, k), "w_i8")
-    _shape(a_scale, (m, _scale_cols(k, a_group)), "a_scale")
-    _shape(w_scale, (n, k // 32), "w_scale")
-    _shape(out, (m, n), "out")
+    _shape(a_i8, (m, k), "a_i8", BYTES)
+    _shape(w_i8, (n, k), "w_i8", BYTES)
+    _shape(a_scale, (m, _scale_cols(k, a_group)), "a_scale", F32)
+    _shape(w_scale, (n, k // 32), "w_scale", F32)
+    _shape(out, (m, n), "out", BF16)
     st = lib().int8_gemm_blockscaled_agroup(_ptr(a_i8), _ptr(w_i8), _ptr(a_scale), int(a_group), _ptr(w_scale),
                                             _ptr(out), m, n, k, _stream(stream, out), int(path))
     _done(st, "int8_gemm_blockscaled_agroup")

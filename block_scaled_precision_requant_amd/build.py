@@ -3,9 +3,12 @@
 Every source is compiled by hipcc with IEEE float semantics (no fast-math, no
 FMA contraction unless written, subnormals kept) and without packed-FP32
 instructions, then linked into block_scaled_precision_requant_amd/libbsr.so.
+Symbols are hidden by default: the library exports exactly the functions
+include/bsr.h declares (marked BSR_API there).
 """
 import concurrent.futures
 import os
+import re
 import subprocess
 import sys
 
@@ -20,7 +23,7 @@ ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
@@ -45,13 +48,31 @@ def _compile(src, save_temps):
     return obj
 
 
+def declared_functions():
+    """Names of the functions include/bsr.h declares (each marked BSR_API)."""
+    with open(os.path.join(INCLUDE, "bsr.h")) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    return sorted(re.findall(r"^BSR_API\s+(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+
+
+def _version_script():
+    """Linker version script: the declared functions global, every other symbol
+    (the compiler's per-unit HIP identifiers included) local."""
+    path = os.path.join(BUILD, "libbsr.map")
+    body = "".join(f"    {name};\n" for name in declared_functions())
+    with open(path, "w") as f:
+        f.write("{\n  global:\n" + body + "  local: *;\n};\n")
+    return path
+
+
 def build(verbose: bool = False, save_temps: bool = False) -> str:
     """Compile every kernel source and link libbsr.so; returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(lambda s: _compile(s, save_temps), SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs,
+           f"-Wl,--version-script={_version_script()}", "-o", tmp]
     subprocess.run(cmd, check=True, capture_output=not verbose)
     os.replace(tmp, LIB)
     if verbose:

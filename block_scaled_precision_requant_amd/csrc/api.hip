@@ -60,6 +60,25 @@ int gemm_args_check(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale
     return BSR_OK;
 }
 
+int gemm_launch(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
+                uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                void *stream, int path) {
+    if (int st = check_device()) return st;
+    const bool small = m <= (uint32_t)bsr::kGemvMaxRows;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (path == BSR_PATH_INVARIANT && small)
+        return launched(bsr::launch_gemv_chain(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s));
+    // The automatic path also takes the streamed GEMV for a few tiles of rows
+    // when the grid is narrow (measured faster than the GEMM's small-grid
+    // tiles up to 48 rows at n <= 4096; slower at n = 14336).
+    const bool narrow = bsr::div_up(n, bsr::kGemvCols) <= (uint64_t)bsr::kGemmCus;
+    const bool stream_rows = m <= (uint32_t)bsr::kGemvStreamAutoRows && k % bsr::kGemvStreamKAlign == 0 && narrow;
+    const bool gemv = path == BSR_PATH_GEMV || (path == BSR_PATH_AUTO && (small || stream_rows));
+    if (gemv) return launched(bsr::launch_gemv(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s));
+    return launched(bsr::launch_gemm(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k,
+                                     path != BSR_PATH_INVARIANT, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -114,29 +133,6 @@ int w4a16_gemv(const uint16_t *x_bf16, const uint8_t *w_packed, const uint8_t *w
     if (int st = check_device()) return st;
     return launched(bsr::launch_w4a16(x_bf16, w_packed, w_e4m3, scale2, out, m, n, k, static_cast<hipStream_t>(stream)));
 }
-
-namespace {
-
-int gemm_launch(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
-                uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
-                void *stream, int path) {
-    if (int st = check_device()) return st;
-    const bool small = m <= (uint32_t)bsr::kGemvMaxRows;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (path == BSR_PATH_INVARIANT && small)
-        return launched(bsr::launch_gemv_chain(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s));
-    // The automatic path also takes the streamed GEMV for a few tiles of rows
-    // when the grid is narrow (measured faster than the GEMM's small-grid
-    // tiles up to 48 rows at n <= 4096; slower at n = 14336).
-    const bool narrow = bsr::div_up(n, bsr::kGemvCols) <= (uint64_t)bsr::kGemmCus;
-    const bool stream_rows = m <= (uint32_t)bsr::kGemvStreamAutoRows && k % bsr::kGemvStreamKAlign == 0 && narrow;
-    const bool gemv = path == BSR_PATH_GEMV || (path == BSR_PATH_AUTO && (small || stream_rows));
-    if (gemv) return launched(bsr::launch_gemv(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s));
-    return launched(bsr::launch_gemm(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k,
-                                     path != BSR_PATH_INVARIANT, s));
-}
-
-}  // namespace
 
 int int8_gemm_blockscaled_ex(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
                              const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,

@@ -472,7 +472,6 @@ __host__ __device__ inline StagedGeo staged_geo(uint32_t m, uint32_t bpw) {
     return g;
 }
 
-constexpr uint32_t kLdsBytes = 160 * 1024;           // LDS of a gfx950 workgroup
 constexpr uint32_t kRedBytes = kGemvMaxWaves * 64 * 4 * 4;
 constexpr int kStagedMaxIters = 8;                   // iterations per wave (unrolled)
 

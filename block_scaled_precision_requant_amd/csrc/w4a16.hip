@@ -34,8 +34,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kStepK = 128;  // K per super-step
-
 // OCP E4M3 code -> binary32 (exact): exponent and mantissa bits shifted into a
 // binary32 give the value times 2^-120.
 __device__ __forceinline__ float e4m3_value(uint32_t code) {
@@ -97,28 +95,20 @@ __device__ __forceinline__ void wait_vm_le() {
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
 }
 
-// Per-wave LDS region: m activation rows of a_pitch bytes (one pass of
-// super-steps plus 16 bytes, so the 16 lanes of a quarter reading 16 rows at
-// one offset spread over the banks).
-__host__ __device__ inline uint32_t w4_pitch(uint32_t pass_steps) { return pass_steps * kStepK * 2 + 16; }
-
-// VS: every weight row's scales start 16-byte aligned (K % 256 == 0) and
-// every pass starts at an even super-step, so a lane reads its row's scale
-// bytes for a pass with 16-byte loads (8 bytes per super-step); otherwise it
-// reads its own two codes per super-step with 2-byte loads.
-// PS: super-steps per staging pass (at most kW4PassSteps; even when VS).
+// A lane reads its own two E4M3 codes per super-step with 2-byte loads (this
+// kernel runs for K % 256 != 0, where scale rows need not be 16-byte aligned).
+// PS: super-steps per staging pass (at most kW4PassSteps).
 // CT: 16-column tiles per workgroup; each wave runs all CT tiles over its K
 // range with one staged copy of the activations, so larger m (whose
 // activation bytes rival the weight bytes) copies them fewer times.
 // (wp and we are not __restrict__: a restrict-qualified read-only load may be
 // moved past the empty asm statements that keep a pass's loads ahead of its
 // compute.)
-template <bool VS, int PS, int CT>
+template <int PS, int CT>
 __global__ __launch_bounds__(kGemvMaxWaves * 64) void w4a16_kernel(
     const uint16_t *__restrict__ x, const uint8_t *wp, const uint8_t *we,
     float scale2, uint16_t *__restrict__ out, uint32_t m, uint32_t n, uint32_t k, uint32_t steps_per_wave) {
     static_assert(PS >= 1 && PS <= kW4PassSteps, "pass length");
-    static_assert(!VS || PS % 2 == 0, "16-byte scale loads cover two super-steps");
     constexpr uint32_t pass_steps = PS;
     extern __shared__ __attribute__((aligned(1024))) int8_t smem[];
     const int lane = threadIdx.x & 63;
@@ -127,7 +117,7 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void w4a16_kernel(
     const int q = lane >> 4;
     const uint32_t c = lane & 15;
     const uint32_t n0 = blockIdx.x * kGemvCols * CT;
-    const uint32_t nsteps = (k + kStepK - 1) / kStepK;
+    const uint32_t nsteps = (k + kW4StepK - 1) / kW4StepK;
     const uint32_t s_begin = wave * steps_per_wave;
     const uint32_t s_end = min(nsteps, s_begin + steps_per_wave);
     const uint32_t pitch = w4_pitch(pass_steps);
@@ -153,7 +143,7 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void w4a16_kernel(
         for (uint32_t b0 = 0; b0 < a_bytes; b0 += 1024) {
             const uint32_t p = b0 + 16 * lane;
             const uint32_t r = min(p / pitch, m - 1);
-            const uint64_t e = min((uint64_t)p0 * kStepK + (p % pitch) / 2, (uint64_t)k - 8);
+            const uint64_t e = min((uint64_t)p0 * kW4StepK + (p % pitch) / 2, (uint64_t)k - 8);
             if (p < a_bytes)
                 __builtin_amdgcn_global_load_lds(x + (uint64_t)r * k + e, (lds_void *)(la + b0), 16, 0, 0);
         }
@@ -163,41 +153,16 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void w4a16_kernel(
         v4i wv[CT][PS];
         uint32_t sc[CT][PS];
         auto load_w = [&](int ct, int j) {
-            const uint32_t kk = min((p0 + min((uint32_t)j, plen - 1)) * kStepK + 32 * q, k - 32);
+            const uint32_t kk = min((p0 + min((uint32_t)j, plen - 1)) * kW4StepK + 32 * q, k - 32);
             wv[ct][j] = *reinterpret_cast<const v4i *>(wrow[ct] + kk / 2);
         };
-        if constexpr (VS) {
-            // 8 scale bytes per super-step: one 16-byte load per pair of super-steps;
-            // the lane's two codes are bytes 8 j' + 2 q, i.e. dword 2 j' + q / 2
-            v4i sv[CT][PS / 2];
 #pragma unroll
-            for (int h = 0; h < PS / 2; ++h) {
-                const uint32_t g = min((p0 + 2 * h) * 8, k / 16 - 16);
+        for (int j = 0; j < PS; ++j) {
+            const uint32_t g = min(((p0 + min((uint32_t)j, plen - 1)) * kW4StepK + 32 * q) / 16, k / 16 - 2);
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    sv[ct][h] = *reinterpret_cast<const v4i *>(srow[ct] + g);
-                    load_w(ct, 2 * h);
-                    load_w(ct, 2 * h + 1);
-                }
-            }
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                for (int j = 0; j < PS; ++j) {
-                    const uint32_t d0 = (j & 1) ? sv[ct][j / 2].z : sv[ct][j / 2].x;
-                    const uint32_t d1 = (j & 1) ? sv[ct][j / 2].w : sv[ct][j / 2].y;
-                    const uint32_t d = (q >> 1) ? d1 : d0;
-                    sc[ct][j] = (q & 1) ? d >> 16 : d & 0xFFFFu;
-                }
-        } else {
-#pragma unroll
-            for (int j = 0; j < PS; ++j) {
-                const uint32_t g = min(((p0 + min((uint32_t)j, plen - 1)) * kStepK + 32 * q) / 16, k / 16 - 2);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    sc[ct][j] = *reinterpret_cast<const uint16_t *>(srow[ct] + g);
-                    load_w(ct, j);
-                }
+            for (int ct = 0; ct < CT; ++ct) {
+                sc[ct][j] = *reinterpret_cast<const uint16_t *>(srow[ct] + g);
+                load_w(ct, j);
             }
         }
         asm volatile("" ::: "memory");
@@ -205,13 +170,13 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void w4a16_kernel(
         //    until only this pass's weight and scale loads may be outstanding
         //    means the activations are in LDS (the compiler then waits per
         //    super-step for just the loads that super-step reads)
-        wait_vm_le<CT * (VS ? PS + PS / 2 : 2 * PS)>();
+        wait_vm_le<CT * 2 * PS>();
 
         const int8_t *xa = la + arow * pitch + 64 * q;  // this lane's 32 BF16 of a super-step
 #pragma unroll
         for (int j = 0; j < PS; ++j) {
             if ((uint32_t)j >= plen) break;
-            const bool live = (p0 + j) * kStepK + 32 * q < k;  // quarters past K contribute 0
+            const bool live = (p0 + j) * kW4StepK + 32 * q < k;  // quarters past K contribute 0
             if constexpr (CT == 1) {
                 const ByteTable t0 = make_table(sc[0][j] & 0xFFu), t1 = make_table(sc[0][j] >> 8);
                 const uint32_t wd[4] = {(uint32_t)wv[0][j].x, (uint32_t)wv[0][j].y, (uint32_t)wv[0][j].z,
@@ -219,7 +184,7 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void w4a16_kernel(
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const v4i b = decode8(wd[t], t < 2 ? t0 : t1);
-                    v4i a = *reinterpret_cast<const v4i *>(xa + j * (kStepK * 2) + 16 * t);
+                    v4i a = *reinterpret_cast<const v4i *>(xa + j * (kW4StepK * 2) + 16 * t);
                     if (!live) a = v4i{0, 0, 0, 0};
                     acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                                      __builtin_bit_cast(bf16x8, b), acc[0], 0, 0, 0);
@@ -229,7 +194,7 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void w4a16_kernel(
             v4i a[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                a[t] = *reinterpret_cast<const v4i *>(xa + j * (kStepK * 2) + 16 * t);
+                a[t] = *reinterpret_cast<const v4i *>(xa + j * (kW4StepK * 2) + 16 * t);
                 if (!live) a[t] = v4i{0, 0, 0, 0};
             }
 #pragma unroll
@@ -481,58 +446,26 @@ hipError_t launch_w4a16(const uint16_t *x, const uint8_t *w_packed, const uint8_
         if (m <= 8) return launch_w4a16_stream<8>(x, w_packed, w_e4m3, scale2, out, m, n, k, s);
         return launch_w4a16_stream<16>(x, w_packed, w_e4m3, scale2, out, m, n, k, s);
     }
-    // Other K: the register-decode kernel.
-    // Column tiles per workgroup: two from m = 4 on, where the activation
-    // bytes a workgroup stages (2 m per K element) approach the weight bytes
-    // of one 16-column tile (9 per K element) -- if that still leaves a
-    // workgroup for every CU.  Waves per workgroup as for the
-    // int8 GEMV (~24 waves per CU over the launch), at most 16 (and with two
-    // tiles, one of them reduces each tile's partial sums); then the smallest
-    // number of passes whose activation staging fits in LDS.
-    const uint32_t ct = m >= 4 && div_up(n, 2 * kGemvCols) >= (uint64_t)kGemmCus ? 2 : 1;
-    const uint32_t tiles = (uint32_t)div_up(n, kGemvCols * ct);
-    const uint32_t nsteps = (uint32_t)div_up(k, kStepK);
-    uint32_t waves = (uint32_t)div_up(6144, tiles);
-    waves = max(ct, min(waves, (uint32_t)kGemvMaxWaves));
-    waves = min(waves, max(nsteps, ct));
-    const bool vs = k % 256 == 0;  // then nsteps is even
-    uint32_t spw = (uint32_t)div_up(nsteps, waves);
-    if (vs) spw += spw & 1u;  // even: every pass starts at an even super-step
-    waves = max((uint32_t)div_up(nsteps, spw), ct);
-    const uint32_t red = ct * kGemvMaxWaves * 64 * 4 * 4;
-    // pass length: the whole per-wave range when its staging fits in LDS,
-    // else the largest that fits (even when the scales are read 16 bytes at a
-    // time); launched with PS rounded up to an instantiated length
-    uint32_t pass = min(spw, ct == 2 ? 6u : (uint32_t)kW4PassSteps);  // two tiles: 6 keeps 128 VGPRs
-    const uint32_t step = vs ? 2u : 1u;
-    while (pass > step && (uint64_t)waves * m * w4_pitch(pass) > 160 * 1024) pass -= step;
-    pass = vs ? max(2u, (pass + 1) & ~1u) : (pass <= 2 ? pass : (pass + 1) & ~1u);
-    const uint32_t lds = max((uint32_t)(waves * m * w4_pitch(pass)), red);
-    if (lds > 160 * 1024) return hipErrorInvalidValue;
-#define BSR_W4_LAUNCH(V, P, C)                                                                            \
-    hipLaunchKernelGGL((w4a16_kernel<V, P, C>), dim3(tiles), dim3(64 * waves), lds, s, x, w_packed, w_e4m3, \
-                       scale2, out, m, n, k, spw)
-    if (ct == 2) {
-        switch ((vs ? 16 : 0) + pass) {
-        case 16 + 6: BSR_W4_LAUNCH(true, 6, 2); break;
-        case 16 + 4: BSR_W4_LAUNCH(true, 4, 2); break;
-        case 16 + 2: BSR_W4_LAUNCH(true, 2, 2); break;
-        case 6: BSR_W4_LAUNCH(false, 6, 2); break;
-        case 4: BSR_W4_LAUNCH(false, 4, 2); break;
-        case 2: BSR_W4_LAUNCH(false, 2, 2); break;
-        default: BSR_W4_LAUNCH(false, 1, 2); break;
+    // Other K: the register-decode kernel, with the plan of bsr_geometry.h.
+    const W4Plan p = w4a16_reg_plan(m, n, k);
+    if (p.lds > kLdsBytes) return hipErrorInvalidValue;
+#define BSR_W4_LAUNCH(P, C)                                                                                 \
+    hipLaunchKernelGGL((w4a16_kernel<P, C>), dim3(p.tiles), dim3(64 * p.waves), p.lds, s, x, w_packed, w_e4m3, \
+                       scale2, out, m, n, k, p.spw)
+    if (p.ct == 2) {
+        switch (p.pass) {
+        case 6: BSR_W4_LAUNCH(6, 2); break;
+        case 4: BSR_W4_LAUNCH(4, 2); break;
+        case 2: BSR_W4_LAUNCH(2, 2); break;
+        default: BSR_W4_LAUNCH(1, 2); break;
         }
     } else {
-        switch ((vs ? 16 : 0) + pass) {
-        case 16 + 8: BSR_W4_LAUNCH(true, 8, 1); break;
-        case 16 + 6: BSR_W4_LAUNCH(true, 6, 1); break;
-        case 16 + 4: BSR_W4_LAUNCH(true, 4, 1); break;
-        case 16 + 2: BSR_W4_LAUNCH(true, 2, 1); break;
-        case 8: BSR_W4_LAUNCH(false, 8, 1); break;
-        case 6: BSR_W4_LAUNCH(false, 6, 1); break;
-        case 4: BSR_W4_LAUNCH(false, 4, 1); break;
-        case 2: BSR_W4_LAUNCH(false, 2, 1); break;
-        default: BSR_W4_LAUNCH(false, 1, 1); break;
+        switch (p.pass) {
+        case 8: BSR_W4_LAUNCH(8, 1); break;
+        case 6: BSR_W4_LAUNCH(6, 1); break;
+        case 4: BSR_W4_LAUNCH(4, 1); break;
+        case 2: BSR_W4_LAUNCH(2, 1); break;
+        default: BSR_W4_LAUNCH(1, 1); break;
         }
     }
 #undef BSR_W4_LAUNCH

@@ -50,6 +50,14 @@
 
 #include <stdint.h>
 
+/* The library is built with hidden visibility: exactly the functions declared
+ * here are exported from libbsr.so. */
+#if defined(__GNUC__) || defined(__clang__)
+#define BSR_API __attribute__((visibility("default")))
+#else
+#define BSR_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -77,8 +85,8 @@ enum bsr_status {
  * Errors: BSR_EINVAL (k, or scale2 not finite), BSR_ENULL, BSR_EALIGN,
  * BSR_EDEVICE, BSR_ELAUNCH.
  */
-int requant_w_nvfp4_int8(const uint8_t *w_packed, const uint8_t *w_e4m3, float scale2,
-                         int8_t *w_i8, float *w_scale, uint32_t n, uint32_t k, void *stream);
+BSR_API int requant_w_nvfp4_int8(const uint8_t *w_packed, const uint8_t *w_e4m3, float scale2,
+                                 int8_t *w_i8, float *w_scale, uint32_t n, uint32_t k, void *stream);
 
 /*
  * Step 2, per-call activation requant (page ".../gemm_dense_int8.rs", doc of
@@ -88,8 +96,8 @@ int requant_w_nvfp4_int8(const uint8_t *w_packed, const uint8_t *w_e4m3, float s
  *   a_scale [m, k/32] f32 output;        4-byte aligned (caller-owned scratch)
  * Errors: BSR_EINVAL, BSR_ENULL, BSR_EALIGN, BSR_EDEVICE, BSR_ELAUNCH.
  */
-int requant_a_int8(const uint16_t *a_bf16, int8_t *a_i8, float *a_scale,
-                   uint32_t m, uint32_t k, void *stream);
+BSR_API int requant_a_int8(const uint16_t *a_bf16, int8_t *a_i8, float *a_scale,
+                           uint32_t m, uint32_t k, void *stream);
 
 /*
  * Step 3, block-scaled GEMM (page ".../gemm_dense_int8.rs", doc of
@@ -107,9 +115,9 @@ int requant_a_int8(const uint16_t *a_bf16, int8_t *a_i8, float *a_scale,
  * workgroups at most one per CU); other shapes run the MFMA GEMM.
  * Errors: BSR_EINVAL, BSR_ENULL, BSR_EALIGN, BSR_EDEVICE, BSR_ELAUNCH.
  */
-int int8_gemm_blockscaled(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
-                          const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
-                          uint32_t k, void *stream);
+BSR_API int int8_gemm_blockscaled(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
+                                  const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
+                                  uint32_t k, void *stream);
 
 /* Paths of int8_gemm_blockscaled_ex. */
 enum bsr_path {
@@ -132,9 +140,9 @@ enum bsr_path {
  * int8_gemm_blockscaled with an explicit path, so tests can run both kernels
  * on the same rows (same arguments and errors; BSR_EINVAL for an unknown path).
  */
-int int8_gemm_blockscaled_ex(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
-                             const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
-                             uint32_t k, void *stream, int path);
+BSR_API int int8_gemm_blockscaled_ex(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
+                                     const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
+                                     uint32_t k, void *stream, int path);
 
 /*
  * Fused SiLU·mul -> int8 per-32 requant: the quantized input of the down
@@ -155,8 +163,8 @@ int int8_gemm_blockscaled_ex(const int8_t *a_i8, const int8_t *w_i8, const float
  * Errors: BSR_EINVAL (k, ld < k, ld not a multiple of 8), BSR_ENULL,
  * BSR_EALIGN, BSR_EDEVICE, BSR_ELAUNCH.
  */
-int silu_mul_requant_int8(const uint16_t *gate, const uint16_t *up, uint32_t ld, int8_t *a_i8,
-                          float *a_scale, uint32_t m, uint32_t k, void *stream);
+BSR_API int silu_mul_requant_int8(const uint16_t *gate, const uint16_t *up, uint32_t ld, int8_t *a_i8,
+                                  float *a_scale, uint32_t m, uint32_t k, void *stream);
 
 /*
  * W4A16 decode GEMV straight from the NVFP4 weight, no int8 requant (the
@@ -176,8 +184,8 @@ int silu_mul_requant_int8(const uint16_t *gate, const uint16_t *up, uint32_t ld,
  * Errors: BSR_EINVAL (k, m > 16, scale2 not finite), BSR_ENULL, BSR_EALIGN,
  * BSR_EDEVICE, BSR_ELAUNCH.
  */
-int w4a16_gemv(const uint16_t *x_bf16, const uint8_t *w_packed, const uint8_t *w_e4m3, float scale2,
-               uint16_t *out, uint32_t m, uint32_t n, uint32_t k, void *stream);
+BSR_API int w4a16_gemv(const uint16_t *x_bf16, const uint8_t *w_packed, const uint8_t *w_e4m3, float scale2,
+                       uint16_t *out, uint32_t m, uint32_t n, uint32_t k, void *stream);
 
 /* Activation code formats of quantize_act. */
 enum bsr_format {
@@ -203,8 +211,8 @@ enum bsr_format {
  * Errors: BSR_EINVAL (k, group, format), BSR_ENULL, BSR_EALIGN, BSR_EDEVICE,
  * BSR_ELAUNCH.
  */
-int quantize_act(const uint16_t *a_bf16, uint8_t *q, float *scale, uint32_t m, uint32_t k,
-                 uint32_t group, int format, void *stream);
+BSR_API int quantize_act(const uint16_t *a_bf16, uint8_t *q, float *scale, uint32_t m, uint32_t k,
+                         uint32_t group, int format, void *stream);
 
 /*
  * int8_gemm_blockscaled_ex with int8 activations whose scales come per group
@@ -218,12 +226,12 @@ int quantize_act(const uint16_t *a_bf16, uint8_t *q, float *scale, uint32_t m, u
  * or as int8_gemm_blockscaled_ex), BSR_ENULL, BSR_EALIGN, BSR_EDEVICE,
  * BSR_ELAUNCH.
  */
-int int8_gemm_blockscaled_agroup(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
-                                 uint32_t a_group, const float *w_scale, uint16_t *out, uint32_t m,
-                                 uint32_t n, uint32_t k, void *stream, int path);
+BSR_API int int8_gemm_blockscaled_agroup(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
+                                         uint32_t a_group, const float *w_scale, uint16_t *out, uint32_t m,
+                                         uint32_t n, uint32_t k, void *stream, int path);
 
 /* Human-readable name of a status code (static storage, never NULL). */
-const char *bsr_status_string(int status);
+BSR_API const char *bsr_status_string(int status);
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,15 @@ from block_scaled_precision_requant_amd import bsr
 
 DEV = torch.device("cuda:0")
 
+# Outputs are pre-filled with a quiet-NaN BF16 pattern: the kernels write finite
+# values only, and the pass rule rejects non-finite outputs, so an element a
+# launch never wrote fails every comparison that covers it.
+CANARY = 0x7FA5
+
+
+def canary_out(m, n):
+    return torch.full((m, n), CANARY, dtype=torch.int16, device=DEV)
+
 
 def say(*args):
     print(*args, flush=True)
@@ -41,7 +50,7 @@ def gpu_requant_a(a_bits):
 def gpu_gemm(a_i8, w_i8, a_s, w_s, path=bsr.PATH_AUTO):
     m = a_i8.shape[0]
     n = w_i8.shape[0]
-    out = torch.empty((m, n), dtype=torch.int16, device=DEV)
+    out = canary_out(m, n)
     bsr.int8_gemm_blockscaled_ex(a_i8, w_i8, a_s, w_s, out, path=path)
     return out
 
@@ -71,7 +80,7 @@ def gpu_w4a16(x_bits, packed, e4m3, scale2):
     x = to_dev(x_bits.view(np.int16))
     wp, we = to_dev(packed), to_dev(e4m3)
     m, n = x.shape[0], wp.shape[0]
-    out = torch.empty((m, n), dtype=torch.int16, device=DEV)
+    out = canary_out(m, n)
     bsr.w4a16_gemv(x, wp, we, float(scale2), out)
     return out
 
@@ -89,6 +98,6 @@ def gpu_quant_act(a_bits, group, fmt=bsr.FMT_INT8):
 def gpu_gemm_agroup(a_i8, w_i8, a_s, group, w_s, path=bsr.PATH_AUTO):
     m = a_i8.shape[0]
     n = w_i8.shape[0]
-    out = torch.empty((m, n), dtype=torch.int16, device=DEV)
+    out = canary_out(m, n)
     bsr.int8_gemm_blockscaled_agroup(a_i8, w_i8, a_s, group, w_s, out, path=path)
     return out

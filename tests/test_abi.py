@@ -16,19 +16,20 @@ HEADER = os.path.join(ROOT, "include", "bsr.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+    return set(re.findall(r"^\s*(?:BSR_API\s+)?(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
 
 
 def test_header_declares_the_entry_points():
     assert _declared_functions() == set(bsr.SIGNATURES)
 
 
-def test_library_exports_every_declared_symbol():
+def test_library_exports_exactly_the_declared_symbols():
     out = subprocess.run(["nm", "-D", "--defined-only", bsr.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
-    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
-    missing = _declared_functions() - exported
-    assert not missing, missing
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    # every dynamic symbol the library defines is a declared entry point: no
+    # internal launcher, helper or compiler-generated symbol leaks out
+    assert exported == _declared_functions(), (exported ^ _declared_functions())
     L = bsr.lib()
     for name in _declared_functions():
         assert getattr(L, name) is not None
@@ -146,3 +147,40 @@ def test_gemm_agroup_validation():
     assert L.int8_gemm_blockscaled_agroup(*args, 128, FAKE, FAKE, 0, 4, 256, None, 0) == bsr.BSR_OK
     assert L.int8_gemm_blockscaled_agroup(FAKE, FAKE, None, 128, FAKE, FAKE, 4, 4, 256, None, 0) == bsr.BSR_ENULL
     assert L.int8_gemm_blockscaled_agroup(FAKE, FAKE, _fake(2), 0, FAKE, FAKE, 4, 4, 256, None, 0) == bsr.BSR_EALIGN
+
+
+def test_binding_rejects_wrong_element_types():
+    """The binding checks each argument's element type before anything reaches the
+    library: a 1-byte output where BF16 is written, or 16-bit scales where binary32
+    scales are read, would make a kernel access memory past the tensor's end."""
+    import torch
+    m, n, k = 4, 8, 64
+    a = torch.zeros((m, k), dtype=torch.int8)
+    w = torch.zeros((n, k), dtype=torch.int8)
+    a_s = torch.zeros((m, k // 32), dtype=torch.float32)
+    w_s = torch.zeros((n, k // 32), dtype=torch.float32)
+    out = torch.zeros((m, n), dtype=torch.int16)
+    bad_cases = [
+        (dict(out=torch.zeros((m, n), dtype=torch.uint8)), "out"),
+        (dict(a_scale=torch.zeros((m, k // 32), dtype=torch.bfloat16)), "a_scale"),
+        (dict(w_scale=torch.zeros((n, k // 32), dtype=torch.float64)), "w_scale"),
+        (dict(a_i8=torch.zeros((m, k), dtype=torch.int16)), "a_i8"),
+    ]
+    for change, what in bad_cases:
+        args = dict(a_i8=a, w_i8=w, a_scale=a_s, w_scale=w_s, out=out)
+        args.update(change)
+        with pytest.raises(ValueError, match=f"{what}: dtype"):
+            bsr.int8_gemm_blockscaled(**args)
+    with pytest.raises(ValueError, match="a_scale: dtype"):
+        bsr.requant_a_int8(torch.zeros((m, k), dtype=torch.bfloat16), a,
+                           torch.zeros((m, k // 32), dtype=torch.float16))
+    with pytest.raises(ValueError, match="w_scale: dtype"):
+        bsr.requant_w_nvfp4_int8(torch.zeros((n, k // 2), dtype=torch.uint8),
+                                 torch.zeros((n, k // 16), dtype=torch.uint8), 1.0, w,
+                                 torch.zeros((n, k // 32), dtype=torch.int32))
+    with pytest.raises(ValueError, match="out: dtype"):
+        bsr.w4a16_gemv(torch.zeros((m, k), dtype=torch.bfloat16), torch.zeros((n, k // 2), dtype=torch.uint8),
+                       torch.zeros((n, k // 16), dtype=torch.uint8), 1.0, torch.zeros((m, n), dtype=torch.float32))
+    # the right element types pass the checks and stop only at the device check
+    with pytest.raises(ValueError, match="device tensor"):
+        bsr.int8_gemm_blockscaled(a, w, a_s, w_s, out)

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from block_scaled_precision_requant_amd import bsr, inputs
-from gpu_util import DEV, gpu_gemm, gpu_requant_a, gpu_requant_w, host, say, to_dev
+from gpu_util import CANARY, DEV, canary_out, gpu_gemm, gpu_requant_a, gpu_requant_w, host, say, to_dev
 from oracle.compare import bf16_ulp, bf16_bits_to_f64, check_bf16
 
 pytestmark = pytest.mark.gpu
@@ -68,6 +68,8 @@ def test_gemm_big_tiles_ragged():
     bsr.int8_gemm_blockscaled_ex(to_dev(a), to_dev(w), to_dev(a_s), to_dev(w_s), out, path=bsr.PATH_GEMM)
     hb = host(buf)
     assert np.all(hb[:pad] == 0x7B7B) and np.all(hb[pad + m * n:] == 0x7B7B)
+    # ... and every element inside was written (0x7B7B, ~2^119, is far above any result here)
+    assert not np.any(hb[pad:pad + m * n] == 0x7B7B)
     rows = np.array([0, 1, 127, 128, 555, 1023, 1024, 1050, 1098, 1099])
     y, t = oracle.gemm_ref(a[rows], w, a_s[rows], w_s)
     _check(f"gemm big tiles {m}x{n}x{k}, rows {rows.tolist()}",
@@ -165,13 +167,24 @@ def test_a6_worked_example_on_gpu():
         assert int(out[0, 0]) == expect
 
 
-def _sample_rows(m, count, seed):
+def _tile_rows(m, per_tile, seed, tile=128):
+    """`per_tile` distinct seeded rows inside every `tile`-row band of the output
+    (offsets differ from band to band), plus the first and the last row."""
     rng = np.random.default_rng(seed)
-    fixed = [0, 1, m // 2, m - 2, m - 1, 127, 128, min(255, m - 1)]
-    rows = set(r for r in fixed if 0 <= r < m)
-    while len(rows) < min(count, m):
-        rows.add(int(rng.integers(0, m)))
+    rows = {0, m - 1}
+    for t0 in range(0, m, tile):
+        h = min(tile, m - t0)
+        for off in rng.choice(h, size=min(per_tile, h), replace=False):
+            rows.add(t0 + int(off))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def test_tile_rows_cover_every_band():
+    rows = _tile_rows(8192, 2, 4)
+    bands = np.unique(rows // 128)
+    assert len(bands) == 64 and len(rows) >= 128
+    offsets = rows % 128
+    assert len(np.unique(offsets)) > 32          # the offset varies from band to band
 
 
 def _prefill_projections():
@@ -181,24 +194,40 @@ def _prefill_projections():
     return out
 
 
+# Workloads the oracle evaluates in full (the tiny and attention-projection
+# ones: 2048 x 4096 x 4096 takes about a second on the host); the others on
+# seeded rows in every 128-row tile band: 4 per band for the dense FFN's two
+# projections (M = 4096: 128 rows + the ends), 3 for the large one (M = 8192:
+# 192 rows + the ends).
+FULL_ORACLE = {"tiny", "attn_proj"}
+
+
 @pytest.mark.parametrize("proj", _prefill_projections(), ids=lambda p: p.name)
-def test_prefill_workload_sampled_rows(proj):
-    """Full-size requant + GEMM on the GPU in the benchmark's launch configuration;
-    the oracle recomputes sampled rows from the same seeded inputs."""
+def test_prefill_workload(proj):
+    """Full-size requant + GEMM on the GPU in the benchmark's launch configuration,
+    the output pre-filled with a canary: every element must be overwritten, and the
+    oracle recomputes every row (small workloads) or seeded rows in every tile band
+    from the same seeded inputs."""
     say(f"prefill {proj.name} m={proj.m} n={proj.n} k={proj.k}")
     packed, e4m3 = proj.weight()
     a = proj.activations()
     w_i8, w_s = gpu_requant_w(packed, e4m3, proj.scale2)
     a_i8, a_s = gpu_requant_a(a)
-    out = gpu_gemm(a_i8, w_i8, a_s, w_s)
+    out = canary_out(proj.m, proj.n)
+    bsr.int8_gemm_blockscaled(a_i8, w_i8, a_s, w_s, out)
     out_h = host(out)
     del out, w_i8, w_s, a_i8, a_s
     torch.cuda.empty_cache()
-    rows = _sample_rows(proj.m, 16 if proj.m * proj.n * proj.k > 1e12 else 32, proj.seed)
+    unwritten = int(np.count_nonzero(out_h == CANARY))
+    assert unwritten == 0, f"{unwritten} output elements never written"
+    if proj.name in FULL_ORACLE:
+        rows = np.arange(proj.m)
+    else:
+        rows = _tile_rows(proj.m, 4 if proj.m <= 4096 else 3, proj.seed)
     ow, osw = oracle.requant_w(packed, e4m3, proj.scale2)
     oa, osa = oracle.requant_a(a[rows])
     y, t = oracle.gemm_ref(oa, ow, osa, osw)
-    _check(f"prefill {proj.name} rows {len(rows)}", out_h[rows], y, t, proj.k)
+    _check(f"prefill {proj.name} rows {len(rows)} of {proj.m}", out_h[rows], y, t, proj.k)
 
 
 @pytest.mark.parametrize("proj", inputs.workload("decode").projections, ids=lambda p: p.name)

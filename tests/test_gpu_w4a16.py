@@ -45,6 +45,20 @@ def test_random_shapes(m, n, k):
     _check(f"w4a16 {m}x{n}x{k}", out, y, t, k)
 
 
+# Register-decode shapes whose largest fitting staging pass is odd (3, 5, 7
+# super-steps): the launch plan rounds it down to an instantiated length
+# inside the 160 KB LDS (rounding up once asked for 165-200 KB and failed).
+@pytest.mark.parametrize("m,n,k", [(12, 4096, 6016), (7, 4096, 9856), (5, 4096, 13696)])
+def test_register_decode_odd_pass_shapes(m, n, k):
+    say(f"w4a16 odd-pass plan m={m} n={n} k={k}")
+    rng = np.random.default_rng(m * 131 + k)
+    x = inputs.bf16_normal(rng, m, k)
+    wp, we = _weight(rng, n, k)
+    y, t = oracle.w4a16_ref(x, wp, we, inputs.SCALE2_1_448)
+    out = host(gpu_w4a16(x, wp, we, inputs.SCALE2_1_448))
+    _check(f"w4a16 {m}x{n}x{k}", out, y, t, k)
+
+
 @pytest.mark.parametrize("proj", inputs.workload("decode").projections, ids=lambda p: p.name)
 def test_decode_workload_full(proj):
     wp, we = proj.weight()

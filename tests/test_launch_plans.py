@@ -1,0 +1,30 @@
+"""Host-side launch plans, checked on the CPU with the code the launchers run:
+the plan header is plain C++ (no HIP), compiled here with the system C++
+compiler into a small checker."""
+import os
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "block_scaled_precision_requant_amd", "csrc")
+HOST = os.path.join(ROOT, "tests", "host")
+
+
+def _run_checker(name, tmp_path):
+    exe = str(tmp_path / name)
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", f"-I{CSRC}", os.path.join(HOST, name + ".cpp"),
+                    "-o", exe], check=True, capture_output=True, text=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    return r.returncode, r.stdout.strip()
+
+
+def test_w4a16_register_decode_plan_fits_lds(tmp_path):
+    """Every m <= 16 with K % 256 != 0 (the register-decode kernel) gets an
+    instantiated pass length whose activation staging fits the 160 KB LDS --
+    including shapes where the largest fitting pass is odd (e.g. m=12, n=4096,
+    k=6016), which must round down, not up past the LDS size."""
+    rc, out = _run_checker("w4a16_plan_check", tmp_path)
+    assert rc == 0, out
+    assert out.startswith("ok ")
+    assert int(out.split()[1]) > 100000
