@@ -51,6 +51,7 @@ int gemm_args_check(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale
         return BSR_EINVAL;
     if (m == 0 || n == 0) return BSR_OK;
     if (path == BSR_PATH_GEMV && !gemv_rows_ok(m, k)) return BSR_EINVAL;
+    if ((path == BSR_PATH_GEMM || m > (uint32_t)bsr::kGemvMaxRows) && k >= bsr::kGemmMaxK) return BSR_EINVAL;
     if (!a_i8 || !w_i8 || !a_scale || !w_scale || !out) return BSR_ENULL;
     if (!aligned(a_i8, 16) || !aligned(w_i8, 16) || !aligned(a_scale, 4) || !aligned(w_scale, 4) ||
         !aligned(out, 2))

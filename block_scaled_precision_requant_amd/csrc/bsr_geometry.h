@@ -45,6 +45,9 @@ constexpr int kGemmStageBytes = 32 * kGemmStageBlocks;    // 128 bytes of K per 
 constexpr int kGemmGroupM = 8;
 constexpr int kXcds = 8;
 constexpr int kGemmCus = 256;                             // compute units of an MI355X
+// The GEMM stages operands with 32-bit buffer offsets from a tile's first row:
+// the rows of a tile (at most 128) must span less than 4 GiB, so k < 2^25.
+constexpr uint32_t kGemmMaxK = 1u << 25;
 
 // ---- GEMV (m <= 16) -------------------------------------------------------
 // A workgroup owns kGemvCols output columns and splits K over its waves; each

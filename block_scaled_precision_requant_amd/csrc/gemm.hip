@@ -14,10 +14,10 @@
 //
 // Operand staging: a stage is kGemmStageBlocks blocks (128 bytes of every A
 // and W row, i.e. whole cache lines) plus the matching scales, copied straight
-// from global memory into LDS with global_load_lds (no registers held while
-// the copy is in flight) into a ring of RING buffers; the next RING - 1
-// stages are in flight while the current one is computed, with one barrier
-// per stage.
+// from global memory into LDS with buffer loads (no registers held while the
+// copy is in flight, and per-lane offsets fixed for the whole K loop) into a
+// ring of RING buffers; the next RING - 1 stages are in flight while the
+// current one is computed, with one barrier per stage.
 #include "bsr_internal.h"
 
 namespace bsr {
@@ -83,61 +83,101 @@ struct Stage {
     float ws[BN][kGemmStageBlocks];
 };
 
-// Issue one stage's global -> LDS copies.  A wave's copy fills LDS in lane
-// order (16 or 4 bytes per lane); the lane whose LDS slot is (row, slot)
-// fetches chunk slot ^ swz(row).  Rows past M or N re-read the last row (their
-// outputs are never stored); K chunks and scale blocks past the last block
-// re-read the last one, and the compute zeroes the scale product of any block
-// past K.  Scale copies map consecutive lanes to consecutive blocks of a row,
-// so one copy touches 16 rows' worth of contiguous bytes.
-// One tile's copies: NSEGS 1 KB segments of 8 rows x 128 bytes, segment `seg`
-// issued by wave seg % NWAVES (compile-time trip counts, fully unrolled).
-template <int NSEGS, int NWAVES>
-__device__ __forceinline__ void copy_rows(int8_t *dst, const int8_t *src, uint32_t rows_limit,
-                                          uint32_t r0, uint32_t K, uint32_t kb, int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < (NSEGS + NWAVES - 1) / NWAVES; ++i) {
-        const int seg = wave + i * NWAVES;
-        if (NSEGS % NWAVES != 0 && seg >= NSEGS) break;
-        const uint32_t row = seg * kRowsPerCopy + lane / kChunksPerRow;
-        const uint32_t chunk = (lane % kChunksPerRow) ^ chunk_swz(row);
-        const uint64_t kof = min((uint64_t)kb * 32 + chunk * 16, (uint64_t)K - 16);
-        __builtin_amdgcn_global_load_lds(src + (uint64_t)min(r0 + row, rows_limit - 1) * K + kof,
-                                         (lds_void *)(dst + seg * 1024), 16, 0, 0);
-    }
-}
+// Operand staging: buffer loads straight into LDS.  A wave's copy fills LDS
+// in lane order (16 bytes per lane for operand rows, 4 for scales); the lane
+// whose LDS slot is (row, slot) fetches chunk slot ^ chunk_swz(row), and scale
+// copies map consecutive lanes to the (swizzled) blocks of a row, so one copy
+// touches 16 rows' worth of contiguous bytes.  Every lane's byte offset within
+// its workgroup's rows is fixed for the whole K loop -- only the scalar K
+// offset of a stage changes -- so a stage's copies cost no vector address
+// arithmetic.  Each operand's buffer starts at the workgroup's first row and
+// ends at its last row inside M (N), so rows past the matrix, and K bytes past
+// the last row's end, read as zero (the buffer range check); other bytes past
+// K in a row read the next row's first blocks, whose scale products the
+// compute zeroes.  Offsets are 32-bit: a tile's rows span less than 4 GiB
+// (k < kGemmMaxK, checked before launch).  Block b of an activation-scale row
+// r reads a_s[r * ld + (b >> shift)]: ld = nb, shift = 0 for a scale per
+// block; a scale per 128 elements has ld = nb / 4, shift = 2, one per row
+// ld = 1, shift = 31.
+template <int BM, int BN, int NWAVES>
+struct BufStage {
+    static constexpr int kSegA = BM / kRowsPerCopy, kSegW = BN / kRowsPerCopy;
+    static constexpr int kSegAs = BM * kGemmStageBlocks / 64, kSegWs = BN * kGemmStageBlocks / 64;
+    static constexpr int kNA = (kSegA + NWAVES - 1) / NWAVES, kNW = (kSegW + NWAVES - 1) / NWAVES;
+    static constexpr int kNAs = (kSegAs + NWAVES - 1) / NWAVES, kNWs = (kSegWs + NWAVES - 1) / NWAVES;
+    __amdgpu_buffer_rsrc_t ra, rw, ras, rws;
+    uint32_t oa[kNA], ow[kNW], oas[kNAs], ows[kNWs];
+    uint32_t a_shift;
 
-// One scale tile's copies: NSEGS segments of 64 floats, consecutive lanes on
-// the (swizzled) blocks of a row.  Block b of row r reads src[r * ld + (b >>
-// shift)]: ld = nb, shift = 0 for a scale per block; an activation scale per
-// 128 elements has ld = nb / 4, shift = 2, one per row ld = 1, shift = 31.
-template <int NSEGS, int NWAVES>
-__device__ __forceinline__ void copy_scales(float *dst, const float *src, uint32_t rows_limit,
-                                            uint32_t r0, uint32_t ld, uint32_t shift, uint32_t nb,
-                                            uint32_t kb, int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < (NSEGS + NWAVES - 1) / NWAVES; ++i) {
-        const int seg = wave + i * NWAVES;
-        if (NSEGS % NWAVES != 0 && seg >= NSEGS) break;
-        const uint32_t idx = seg * 64 + lane;  // = row * kGemmStageBlocks + slot
-        const uint32_t row = idx / kGemmStageBlocks;
-        const uint32_t blk = min(kb + ((idx % kGemmStageBlocks) ^ scale_swz(row)), nb - 1);
-        __builtin_amdgcn_global_load_lds(src + (uint64_t)min(r0 + row, rows_limit - 1) * ld + (blk >> shift),
-                                         (lds_void *)(dst + seg * 64), 4, 0, 0);
-    }
-}
+    static constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit elements (gfx9)
 
-template <class G, int BM, int BN>
-__device__ __forceinline__ void issue_stage(Stage<BM, BN> &st, const int8_t *a, const int8_t *w,
-                                            const float *a_s, const float *w_s, uint32_t M,
-                                            uint32_t N, uint32_t K, uint32_t nb, uint32_t a_ld,
-                                            uint32_t a_shift, uint32_t m0, uint32_t n0, uint32_t kb,
-                                            int wave, int lane) {
-    copy_rows<BM / kRowsPerCopy, G::kWaves>(st.a, a, M, m0, K, kb, wave, lane);
-    copy_rows<BN / kRowsPerCopy, G::kWaves>(st.w, w, N, n0, K, kb, wave, lane);
-    copy_scales<BM * kGemmStageBlocks / 64, G::kWaves>(&st.as[0][0], a_s, M, m0, a_ld, a_shift, nb, kb, wave, lane);
-    copy_scales<BN * kGemmStageBlocks / 64, G::kWaves>(&st.ws[0][0], w_s, N, n0, nb, 0, nb, kb, wave, lane);
-}
+    __device__ __forceinline__ void init(const int8_t *a, const int8_t *w, const float *a_s, const float *w_s,
+                                         uint32_t M, uint32_t N, uint32_t K, uint32_t nb, uint32_t a_ld,
+                                         uint32_t shift, uint32_t m0, uint32_t n0, int wave, int lane) {
+        const uint32_t rows_a = min((uint32_t)BM, M - m0), rows_w = min((uint32_t)BN, N - n0);
+        ra = __builtin_amdgcn_make_buffer_rsrc((void *)(a + (uint64_t)m0 * K), (short)0, (int)(rows_a * K), kRsrcWord3);
+        rw = __builtin_amdgcn_make_buffer_rsrc((void *)(w + (uint64_t)n0 * K), (short)0, (int)(rows_w * K), kRsrcWord3);
+        ras = __builtin_amdgcn_make_buffer_rsrc((void *)(a_s + (uint64_t)m0 * a_ld), (short)0, (int)(rows_a * a_ld * 4),
+                                                kRsrcWord3);
+        rws = __builtin_amdgcn_make_buffer_rsrc((void *)(w_s + (uint64_t)n0 * nb), (short)0, (int)(rows_w * nb * 4),
+                                                kRsrcWord3);
+        a_shift = shift;
+#pragma unroll
+        for (int i = 0; i < kNA; ++i) {
+            const uint32_t row = (wave + i * NWAVES) * kRowsPerCopy + lane / kChunksPerRow;
+            oa[i] = row * K + (((lane % kChunksPerRow) ^ chunk_swz(row)) << 4);
+        }
+#pragma unroll
+        for (int i = 0; i < kNW; ++i) {
+            const uint32_t row = (wave + i * NWAVES) * kRowsPerCopy + lane / kChunksPerRow;
+            ow[i] = row * K + (((lane % kChunksPerRow) ^ chunk_swz(row)) << 4);
+        }
+#pragma unroll
+        for (int i = 0; i < kNAs; ++i) {
+            const uint32_t idx = (wave + i * NWAVES) * 64 + lane, row = idx / kGemmStageBlocks;
+            const uint32_t blk = (idx % kGemmStageBlocks) ^ scale_swz(row);
+            oas[i] = row * a_ld * 4 + (shift == 0 ? blk * 4 : 0);
+        }
+#pragma unroll
+        for (int i = 0; i < kNWs; ++i) {
+            const uint32_t idx = (wave + i * NWAVES) * 64 + lane, row = idx / kGemmStageBlocks;
+            const uint32_t blk = (idx % kGemmStageBlocks) ^ scale_swz(row);
+            ows[i] = row * nb * 4 + blk * 4;
+        }
+    }
+
+    // One stage's copies (first block kb): 1 KB per row-segment instruction,
+    // 256 bytes per scale-segment instruction; segment `seg` of an operand is
+    // issued by wave seg % NWAVES.
+    __device__ __forceinline__ void issue(Stage<BM, BN> &st, uint32_t kb, int wave) const {
+#pragma unroll
+        for (int i = 0; i < kNA; ++i) {
+            const int seg = wave + i * NWAVES;
+            if (kSegA % NWAVES != 0 && seg >= kSegA) break;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st.a + seg * 1024), 16, oa[i], kb * 32, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < kNW; ++i) {
+            const int seg = wave + i * NWAVES;
+            if (kSegW % NWAVES != 0 && seg >= kSegW) break;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(st.w + seg * 1024), 16, ow[i], kb * 32, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < kNAs; ++i) {
+            const int seg = wave + i * NWAVES;
+            if (kSegAs % NWAVES != 0 && seg >= kSegAs) break;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_void *)(&st.as[0][0] + seg * 64), 4, oas[i],
+                                                     (kb >> a_shift) * 4, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < kNWs; ++i) {
+            const int seg = wave + i * NWAVES;
+            if (kSegWs % NWAVES != 0 && seg >= kSegWs) break;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rws, (lds_void *)(&st.ws[0][0] + seg * 64), 4, ows[i], kb * 4,
+                                                     0, 0);
+        }
+    }
+};
 
 // Copies one wave issues per stage, when every operand's segments divide
 // evenly among the waves (required for rings deeper than 2, whose waits count
@@ -194,6 +234,10 @@ __device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "
     asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), \
                  "+v"(x[6]), "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]),    \
                  "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15]))
+
+}  // namespace
+
+namespace gemm_kernels {
 
 // KG: K groups.  With KG > 1 the workgroup holds KG copies of the wave grid,
 // each with its own ring, walking its own contiguous range of stages; at the
@@ -322,10 +366,9 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
 #pragma unroll
             for (int j = 0; j < TN; ++j) BSR_PIN16(acc[i][j]);
     };
-    auto issue = [&](St &buf, uint32_t stage) {
-        issue_stage<G>(buf, a, w, a_s, w_s, M, N, K, nb, a_ld, a_shift, m0, n0, (s_first + stage) * kGemmStageBlocks,
-                       wave, lane);
-    };
+    BufStage<BM, BN, G::kWaves> bufst;
+    bufst.init(a, w, a_s, w_s, M, N, K, nb, a_ld, a_shift, m0, n0, wave, lane);
+    auto issue = [&](St &buf, uint32_t stage) { bufst.issue(buf, (s_first + stage) * kGemmStageBlocks, wave); };
     // Stage s lives in buffer s % RING.  At the top of stage s each wave waits
     // for its own copies of stage s (those of the up to RING - 2 later stages
     // already issued may stay in flight), the barrier publishes every wave's
@@ -391,6 +434,27 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
         }
 }
 
+
+// Explicit instantiations of every launched shape: clang otherwise left the
+// host launch symbols of some instantiations undefined.
+#define BSR_GEMM_INST(BM, BN, WM, WN, WGC, KG, RING)                                                        \
+    template __global__ void gemm_kernel<BM, BN, WM, WN, WGC, KG, RING>(                                    \
+        const int8_t *__restrict__, const int8_t *__restrict__, const float *__restrict__,                  \
+        const float *__restrict__, uint16_t *__restrict__, uint32_t, uint32_t, uint32_t, uint32_t, uint32_t, \
+        uint32_t, uint32_t);
+BSR_GEMM_INST(128, 128, 64, 64, 2, 1, 2)
+BSR_GEMM_INST(32, 32, 32, 32, 1, 8, 2)
+BSR_GEMM_INST(32, 32, 32, 32, 2, 4, 2)
+BSR_GEMM_INST(64, 64, 32, 32, 1, 2, 3)
+BSR_GEMM_INST(64, 64, 32, 32, 2, 1, 2)
+#undef BSR_GEMM_INST
+
+}  // namespace gemm_kernels
+
+namespace {
+
+using gemm_kernels::gemm_kernel;
+
 template <int BM, int BN, int WM, int WN, int WG_PER_CU, int KG = 1, int RING = 2>
 hipError_t launch_tiles(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
                         const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
@@ -398,8 +462,8 @@ hipError_t launch_tiles(const int8_t *a_i8, const int8_t *w_i8, const float *a_s
     const uint32_t tiles_m = (uint32_t)div_up(m, BM);
     const uint32_t tiles_n = (uint32_t)div_up(n, BN);
     hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, WG_PER_CU, KG, RING>), dim3(tiles_m * tiles_n),
-                       dim3(Geo<BM, BN, WM, WN>::kThreads * KG), 0, s, a_i8, w_i8, a_scale, w_scale, out, m, n,
-                       k, a_ld, a_shift, tiles_m, tiles_n);
+                       dim3(Geo<BM, BN, WM, WN>::kThreads * KG), 0, s, a_i8, w_i8, a_scale, w_scale, out, m, n, k,
+                       a_ld, a_shift, tiles_m, tiles_n);
     return hipGetLastError();
 }
 

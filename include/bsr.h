@@ -113,7 +113,10 @@ BSR_API int requant_a_int8(const uint16_t *a_bf16, int8_t *a_i8, float *a_scale,
  * m <= 16 (one 16-row matrix-core tile) runs the weight-streaming GEMV; so
  * does m <= 48 when k is a multiple of 256 and n <= 4096 (16-column
  * workgroups at most one per CU); other shapes run the MFMA GEMM.
- * Errors: BSR_EINVAL, BSR_ENULL, BSR_EALIGN, BSR_EDEVICE, BSR_ELAUNCH.
+ * Limit: for m > 16, k < 2^25 (the GEMM addresses a tile's 128 rows with
+ * 32-bit offsets).
+ * Errors: BSR_EINVAL (k; m > 16 with k >= 2^25), BSR_ENULL, BSR_EALIGN,
+ * BSR_EDEVICE, BSR_ELAUNCH.
  */
 BSR_API int int8_gemm_blockscaled(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
                                   const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
@@ -122,7 +125,7 @@ BSR_API int int8_gemm_blockscaled(const int8_t *a_i8, const int8_t *w_i8, const 
 /* Paths of int8_gemm_blockscaled_ex. */
 enum bsr_path {
     BSR_PATH_AUTO = 0, /* as int8_gemm_blockscaled                       */
-    BSR_PATH_GEMM = 1, /* the MFMA GEMM at any m                         */
+    BSR_PATH_GEMM = 1, /* the MFMA GEMM at any m (k < 2^25)              */
     BSR_PATH_GEMV = 2, /* the GEMV; requires m <= 16, or m <= 64 with k a
                         * multiple of 256, else BSR_EINVAL              */
     BSR_PATH_INVARIANT = 3 /* m <= 16: a GEMV that accumulates every output

@@ -184,3 +184,17 @@ def test_binding_rejects_wrong_element_types():
     # the right element types pass the checks and stop only at the device check
     with pytest.raises(ValueError, match="device tensor"):
         bsr.int8_gemm_blockscaled(a, w, a_s, w_s, out)
+
+
+def test_gemm_k_limit():
+    """The GEMM (m > 16, or the GEMM path forced) needs k < 2^25: its staging
+    addresses a tile's 128 rows with 32-bit offsets.  The GEMV (m <= 16) has no
+    such limit, so there validation passes and only the device check answers."""
+    L = bsr.lib()
+    k = 1 << 25
+    assert L.int8_gemm_blockscaled(FAKE, FAKE, FAKE, FAKE, FAKE, 17, 8, k, None) == bsr.BSR_EINVAL
+    assert L.int8_gemm_blockscaled_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, k, None, bsr.PATH_GEMM) == bsr.BSR_EINVAL
+    assert L.int8_gemm_blockscaled_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 40, 8, k, None, bsr.PATH_INVARIANT) == \
+        bsr.BSR_EINVAL
+    assert L.int8_gemm_blockscaled(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, k, None) != bsr.BSR_EINVAL
+    assert L.int8_gemm_blockscaled(FAKE, FAKE, FAKE, FAKE, FAKE, 17, 8, k - 32, None) != bsr.BSR_EINVAL
