@@ -29,6 +29,8 @@ SIGNATURES = {
     "w4a16_gemv": (_int, [_vp, _vp, _vp, _f32, _vp, _u32, _u32, _u32, _vp]),
     "quantize_act": (_int, [_vp, _vp, _vp, _u32, _u32, _u32, _int, _vp]),
     "int8_gemm_blockscaled_agroup": (_int, [_vp, _vp, _vp, _u32, _vp, _vp, _u32, _u32, _u32, _vp, _int]),
+    "int8_gemm_blockscaled_ws_bytes": (ctypes.c_uint64, [_u32, _u32, _u32]),
+    "int8_gemm_blockscaled_ws": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u32, _u32, _vp, ctypes.c_uint64, _vp]),
     "bsr_status_string": (ctypes.c_char_p, [_int]),
 }
 
@@ -187,6 +189,30 @@ def int8_gemm_blockscaled(a_i8, w_i8, a_scale, w_scale, out, stream=None):
     st = lib().int8_gemm_blockscaled(_ptr(a_i8), _ptr(w_i8), _ptr(a_scale), _ptr(w_scale), _ptr(out),
                                      m, n, k, _stream(stream, out))
     _done(st, "int8_gemm_blockscaled")
+
+
+def int8_gemm_blockscaled_ws_bytes(m, n, k):
+    """Workspace bytes int8_gemm_blockscaled_ws needs for (m, n, k); 0 if it runs without a K split."""
+    return int(lib().int8_gemm_blockscaled_ws_bytes(int(m), int(n), int(k)))
+
+
+def int8_gemm_blockscaled_ws(a_i8, w_i8, a_scale, w_scale, out, workspace, stream=None):
+    """int8_gemm_blockscaled with a caller workspace (a 16-byte aligned device
+    tensor of at least int8_gemm_blockscaled_ws_bytes(M, N, K) bytes, or None when
+    that is 0), which lets small grids split K across workgroups."""
+    m, k = a_i8.shape
+    n = w_i8.shape[0]
+    _shape(a_i8, (m, k), "a_i8", BYTES)
+    _shape(w_i8, (n, k), "w_i8", BYTES)
+    _shape(a_scale, (m, k // 32), "a_scale", F32)
+    _shape(w_scale, (n, k // 32), "w_scale", F32)
+    _shape(out, (m, n), "out", BF16)
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace: must be contiguous")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().int8_gemm_blockscaled_ws(_ptr(a_i8), _ptr(w_i8), _ptr(a_scale), _ptr(w_scale), _ptr(out), m, n, k,
+                                        _ptr(workspace), ws_bytes, _stream(stream, out))
+    _done(st, "int8_gemm_blockscaled_ws")
 
 
 FMT_INT8, FMT_E4M3 = 0, 1

@@ -149,6 +149,26 @@ int int8_gemm_blockscaled(const int8_t *a_i8, const int8_t *w_i8, const float *a
     return int8_gemm_blockscaled_ex(a_i8, w_i8, a_scale, w_scale, out, m, n, k, stream, BSR_PATH_AUTO);
 }
 
+uint64_t int8_gemm_blockscaled_ws_bytes(uint32_t m, uint32_t n, uint32_t k) {
+    return bsr::gemm_split_plan(m, n, k).bytes;
+}
+
+int int8_gemm_blockscaled_ws(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
+                             const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                             void *workspace, uint64_t workspace_bytes, void *stream) {
+    if (int st = gemm_args_check(a_i8, w_i8, a_scale, w_scale, out, m, n, k, BSR_PATH_AUTO)) return st;
+    if (m == 0 || n == 0) return BSR_OK;
+    const bsr::SplitPlan plan = bsr::gemm_split_plan(m, n, k);
+    if (plan.slices == 0)
+        return gemm_launch(a_i8, w_i8, a_scale, k / 32, 0, w_scale, out, m, n, k, stream, BSR_PATH_AUTO);
+    if (!workspace) return BSR_ENULL;
+    if (!aligned(workspace, 16)) return BSR_EALIGN;
+    if (workspace_bytes < plan.bytes) return BSR_EINVAL;
+    if (int st = check_device()) return st;
+    return launched(bsr::launch_gemm_split(a_i8, w_i8, a_scale, w_scale, out, m, n, k,
+                                           static_cast<float *>(workspace), plan, static_cast<hipStream_t>(stream)));
+}
+
 int int8_gemm_blockscaled_agroup(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
                                  uint32_t a_group, const float *w_scale, uint16_t *out, uint32_t m,
                                  uint32_t n, uint32_t k, void *stream, int path) {

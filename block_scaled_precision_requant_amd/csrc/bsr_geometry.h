@@ -76,6 +76,52 @@ inline uint64_t div_up(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
 constexpr uint32_t kLdsBytes = 160u * 1024u;  // LDS of one CU (gfx950)
 
+// ---- GEMM with K split across workgroups (caller workspace) ---------------
+// For grids of fewer 64 x 64 tiles than CUs, each tile's K range is cut into
+// `slices` contiguous ranges of whole stages, one workgroup per (tile, slice);
+// every slice writes its FP32 tile to the workspace ([slice][m][n], each
+// slice `pitch` floats), and a second kernel adds the slices in slice order
+// and rounds to BF16.  slices * tiles <= kSplitMaxWorkgroups, so the
+// workspace never exceeds kSplitMaxWorkgroups * 64 * 64 * 4 bytes (8 MiB).
+constexpr uint32_t kSplitTile = 64;
+constexpr uint32_t kSplitMaxWorkgroups = 2 * kGemmCus;  // two workgroups per CU
+constexpr uint32_t kSplitMaxSlices = 16;
+constexpr uint32_t kSplitMinStages = 4;                 // K stages per slice, at least
+// Where the split measured faster than the paths without workspace: more
+// rows than the streamed GEMV's two 16-row tiles, and K long enough (64
+// stages, K >= 8192) to hide each slice's pipeline start and the second
+// launch (n = 4096, k = 14336: m = 48 / 64 / 128 / 192 in 25.5 / 27.0 / 39.3 /
+// 60.2 us against 26.6 / 33.8 / 54.1 / 67.3; n = 14336, k = 4096, m = 17-64:
+// 1.4-1.8 us slower; m = 17-32 at n = 4096: 1.7-3.3 us slower).
+constexpr uint32_t kSplitMinRows = 33;
+constexpr uint32_t kSplitMinKStages = 64;
+constexpr uint64_t kSplitMaxBytes = (uint64_t)kSplitMaxWorkgroups * kSplitTile * kSplitTile * 4;
+
+struct SplitPlan {
+    uint32_t slices;       // 0: no split (the ordinary paths run)
+    uint32_t stages;       // K stages (of kGemmStageBlocks blocks) per slice
+    uint64_t pitch;        // floats per slice in the workspace (m * n rounded up to 4)
+    uint64_t bytes;        // workspace bytes the split needs
+};
+
+inline SplitPlan gemm_split_plan(uint32_t m, uint32_t n, uint32_t k) {
+    SplitPlan p{0, 0, 0, 0};
+    if (m < kSplitMinRows || k == 0 || k % 32 != 0) return p;
+    const uint64_t tiles = div_up(m, kSplitTile) * div_up(n, kSplitTile);
+    const uint32_t stages = (uint32_t)div_up(k / 32, kGemmStageBlocks);
+    if (tiles >= (uint64_t)kGemmCus || stages < kSplitMinKStages) return p;
+    uint64_t s = kSplitMaxWorkgroups / tiles;
+    s = s < kSplitMaxSlices ? s : kSplitMaxSlices;
+    s = s < stages / kSplitMinStages ? s : stages / kSplitMinStages;
+    if (s < 2) return p;
+    p.stages = (uint32_t)div_up(stages, s);
+    p.slices = (uint32_t)div_up(stages, p.stages);  // every slice non-empty
+    if (p.slices < 2) return SplitPlan{0, 0, 0, 0};
+    p.pitch = ((uint64_t)m * n + 3) & ~(uint64_t)3;
+    p.bytes = (uint64_t)p.slices * p.pitch * 4;
+    return p;
+}
+
 // ---- W4A16 register-decode kernel (K % 256 != 0) --------------------------
 constexpr int kW4StepK = 128;  // K per super-step
 

@@ -245,11 +245,17 @@ namespace gemm_kernels {
 // splits K inside a workgroup (no memory beyond the output) for grids too
 // small to fill the CUs; the per-output order is then the groups' sum of
 // sequential chains, so the path-invariant mode keeps KG = 1.
-template <int BM, int BN, int WM, int WN, int WG_PER_CU, int KG, int RING>
+// SPLIT: K split across workgroups.  Workgroup g runs tile g % tiles over the
+// slice_stages stages of slice g / tiles and writes its FP32 tile to
+// partial[slice * pitch + row * N + col] instead of BF16 out; the slices are
+// added in slice order by split_reduce_kernel.
+template <int BM, int BN, int WM, int WN, int WG_PER_CU, int KG, int RING, bool SPLIT>
 __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm_kernel(
     const int8_t *__restrict__ a, const int8_t *__restrict__ w, const float *__restrict__ a_s,
     const float *__restrict__ w_s, uint16_t *__restrict__ out, uint32_t M, uint32_t N, uint32_t K,
-    uint32_t a_ld, uint32_t a_shift, uint32_t tiles_m, uint32_t tiles_n) {
+    uint32_t a_ld, uint32_t a_shift, uint32_t tiles_m, uint32_t tiles_n, float *__restrict__ partial,
+    uint64_t pitch, uint32_t slice_stages) {
+    static_assert(!(SPLIT && KG > 1), "one K split at a time");
     using G = Geo<BM, BN, WM, WN>;
     constexpr int TM = G::kTM, TN = G::kTN;
     using St = Stage<BM, BN>;
@@ -267,18 +273,24 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
     const int wave = wave_all % G::kWaves;     // wave within the group's grid
     St *ring = rings[grp];
     const int wm = wave / G::kWavesN, wn = wave % G::kWavesN;
-    uint32_t tm, tn;
-    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    uint32_t tm, tn, tile = blockIdx.x, slice = 0;
+    if constexpr (SPLIT) {
+        slice = blockIdx.x / (tiles_m * tiles_n);
+        tile = blockIdx.x % (tiles_m * tiles_n);
+    }
+    tile_of(tile, tiles_m, tiles_n, tm, tn);
     const uint32_t m0 = tm * BM, n0 = tn * BN;
     const uint32_t nb = K / 32;
     const uint32_t all_stages = (nb + kGemmStageBlocks - 1) / kGemmStageBlocks;
-    // this group's stages [s_first, s_first + nstages); every group steps
-    // through spg barriers, so groups with fewer stages idle in their tail
-    // (KG == 1: the whole K, with the bounds folded to constants of the loop)
-    const uint32_t spg = KG == 1 ? all_stages : (all_stages + KG - 1) / KG;
-    const uint32_t s_first = KG == 1 ? 0 : min(grp * spg, all_stages);
-    const uint32_t nstages = KG == 1 ? all_stages : min(spg, all_stages - s_first);
-    const uint32_t kend = KG == 1 ? nb : min(nb, (s_first + nstages) * kGemmStageBlocks);  // blocks past it add nothing
+    // this group's (slice's) stages [s_first, s_first + nstages); every group
+    // steps through spg barriers, so groups with fewer stages idle in their
+    // tail (no split: the whole K, with the bounds folded to constants of the
+    // loop)
+    constexpr bool kRange = KG > 1 || SPLIT;
+    const uint32_t spg = SPLIT ? slice_stages : (KG == 1 ? all_stages : (all_stages + KG - 1) / KG);
+    const uint32_t s_first = SPLIT ? slice * slice_stages : (KG == 1 ? 0 : min(grp * spg, all_stages));
+    const uint32_t nstages = kRange ? min(spg, all_stages - min(s_first, all_stages)) : all_stages;
+    const uint32_t kend = kRange ? min(nb, (s_first + nstages) * kGemmStageBlocks) : nb;  // blocks past it add nothing
 
     // Per-lane LDS offsets of the MFMA operands (constant over the K loop):
     // lane l reads row (l % 32) of its 32-row tile and, for block j, the 16-byte
@@ -378,11 +390,11 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
         wait_later_stages<kCopies, RING - 2>(s < nstages ? min(nstages - 1 - s, (uint32_t)RING - 2) : 0);
         stage_barrier();
         if (s + RING - 1 < nstages) issue(ring[(u + RING - 1) % RING], s + RING - 1);
-        if (KG == 1 || s < nstages) compute(ring[u], (s_first + s) * kGemmStageBlocks);
+        if (!kRange || s < nstages) compute(ring[u], (s_first + s) * kGemmStageBlocks);
     };
 #pragma unroll
     for (int r = 0; r < RING - 1; ++r)
-        if ((KG == 1 && r == 0) || (uint32_t)r < nstages) issue(ring[r], r);  // (KG == 1: K has a stage)
+        if ((!kRange && r == 0) || (uint32_t)r < nstages) issue(ring[r], r);  // (no split: K has a stage)
     for (uint32_t s = 0; s < spg; s += RING) {
 #pragma unroll
         for (int u = 0; u < RING; ++u) {
@@ -429,24 +441,53 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const uint32_t row = m0 + wm * WM + sm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (row < M && col < N) out[(uint64_t)row * N + col] = f32_to_bf16_rne(acc[sm][sn][r]);
+                if (row < M && col < N) {
+                    if constexpr (SPLIT)
+                        partial[slice * pitch + (uint64_t)row * N + col] = acc[sm][sn][r];
+                    else
+                        out[(uint64_t)row * N + col] = f32_to_bf16_rne(acc[sm][sn][r]);
+                }
             }
         }
+}
+
+// The K slices of a split GEMM: out = bf16_rne(((p_0 + p_1) + p_2) + ...), the
+// FP32 slice tiles added in slice order (4 consecutive outputs per lane; each
+// slice holds `pitch` floats, m * n rounded up to a multiple of 4).
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restrict__ partial,
+                                                           uint16_t *__restrict__ out, uint64_t mn, uint64_t pitch,
+                                                           uint32_t slices) {
+    const uint64_t i = ((uint64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= mn) return;
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    v4f acc = *reinterpret_cast<const v4f *>(partial + i);
+    for (uint32_t sl = 1; sl < slices; ++sl) {
+        const v4f v = *reinterpret_cast<const v4f *>(partial + sl * pitch + i);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    const float r[4] = {acc.x, acc.y, acc.z, acc.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (i + j < mn) out[i + j] = f32_to_bf16_rne(r[j]);
 }
 
 
 // Explicit instantiations of every launched shape: clang otherwise left the
 // host launch symbols of some instantiations undefined.
-#define BSR_GEMM_INST(BM, BN, WM, WN, WGC, KG, RING)                                                        \
-    template __global__ void gemm_kernel<BM, BN, WM, WN, WGC, KG, RING>(                                    \
+#define BSR_GEMM_INST(BM, BN, WM, WN, WGC, KG, RING, SPLIT)                                                 \
+    template __global__ void gemm_kernel<BM, BN, WM, WN, WGC, KG, RING, SPLIT>(                             \
         const int8_t *__restrict__, const int8_t *__restrict__, const float *__restrict__,                  \
         const float *__restrict__, uint16_t *__restrict__, uint32_t, uint32_t, uint32_t, uint32_t, uint32_t, \
-        uint32_t, uint32_t);
-BSR_GEMM_INST(128, 128, 64, 64, 2, 1, 2)
-BSR_GEMM_INST(32, 32, 32, 32, 1, 8, 2)
-BSR_GEMM_INST(32, 32, 32, 32, 2, 4, 2)
-BSR_GEMM_INST(64, 64, 32, 32, 1, 2, 3)
-BSR_GEMM_INST(64, 64, 32, 32, 2, 1, 2)
+        uint32_t, uint32_t, float *__restrict__, uint64_t, uint32_t);
+BSR_GEMM_INST(128, 128, 64, 64, 2, 1, 2, false)
+BSR_GEMM_INST(32, 32, 32, 32, 1, 8, 2, false)
+BSR_GEMM_INST(32, 32, 32, 32, 2, 4, 2, false)
+BSR_GEMM_INST(64, 64, 32, 32, 1, 2, 3, false)
+BSR_GEMM_INST(64, 64, 32, 32, 2, 1, 2, false)
+BSR_GEMM_INST(64, 64, 32, 32, 2, 1, 4, true)
 #undef BSR_GEMM_INST
 
 }  // namespace gemm_kernels
@@ -454,6 +495,7 @@ BSR_GEMM_INST(64, 64, 32, 32, 2, 1, 2)
 namespace {
 
 using gemm_kernels::gemm_kernel;
+using gemm_kernels::split_reduce_kernel;
 
 template <int BM, int BN, int WM, int WN, int WG_PER_CU, int KG = 1, int RING = 2>
 hipError_t launch_tiles(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
@@ -461,9 +503,9 @@ hipError_t launch_tiles(const int8_t *a_i8, const int8_t *w_i8, const float *a_s
                         uint32_t a_ld, uint32_t a_shift, hipStream_t s) {
     const uint32_t tiles_m = (uint32_t)div_up(m, BM);
     const uint32_t tiles_n = (uint32_t)div_up(n, BN);
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, WG_PER_CU, KG, RING>), dim3(tiles_m * tiles_n),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, WG_PER_CU, KG, RING, false>), dim3(tiles_m * tiles_n),
                        dim3(Geo<BM, BN, WM, WN>::kThreads * KG), 0, s, a_i8, w_i8, a_scale, w_scale, out, m, n, k,
-                       a_ld, a_shift, tiles_m, tiles_n);
+                       a_ld, a_shift, tiles_m, tiles_n, nullptr, 0, 0);
     return hipGetLastError();
 }
 
@@ -508,6 +550,24 @@ hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_sc
                                                                              n, k, a_ld, a_shift, s);
     return launch_tiles<kGemmSmallTile, kGemmSmallTile, 32, 32, 2>(a_i8, w_i8, a_scale, w_scale, out, m, n, k,
                                                                    a_ld, a_shift, s);
+}
+
+hipError_t launch_gemm_split(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
+                             const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                             float *partial, const SplitPlan &plan, hipStream_t s) {
+    // 64 x 64 tiles of four 32 x 32 waves, two workgroups per CU, each with a
+    // 4-deep ring (three stages in flight: a slice streams its A and W rows
+    // from HBM with ~54 KB per workgroup outstanding)
+    const uint32_t tiles_m = (uint32_t)div_up(m, kSplitTile), tiles_n = (uint32_t)div_up(n, kSplitTile);
+    const uint32_t grid = tiles_m * tiles_n * plan.slices;
+    hipLaunchKernelGGL((gemm_kernel<kSplitTile, kSplitTile, 32, 32, 2, 1, 4, true>), dim3(grid),
+                       dim3(Geo<kSplitTile, kSplitTile, 32, 32>::kThreads), 0, s, a_i8, w_i8, a_scale, w_scale,
+                       out, m, n, k, k / 32, 0u, tiles_m, tiles_n, partial, plan.pitch, plan.stages);
+    if (hipError_t e = hipGetLastError()) return e;
+    const uint64_t mn = (uint64_t)m * n;
+    hipLaunchKernelGGL(split_reduce_kernel, dim3((uint32_t)div_up(mn, 4 * 256)), dim3(256), 0, s, partial, out, mn,
+                       plan.pitch, plan.slices);
+    return hipGetLastError();
 }
 
 }  // namespace bsr

@@ -148,6 +148,40 @@ BSR_API int int8_gemm_blockscaled_ex(const int8_t *a_i8, const int8_t *w_i8, con
                                      uint32_t k, void *stream, int path);
 
 /*
+ * Workspace bytes int8_gemm_blockscaled_ws needs for an (m, n, k) problem: 0
+ * when that problem runs without a K split (then no workspace is used), else
+ * at most 8 MiB.  Pure host arithmetic, no device call.
+ */
+BSR_API uint64_t int8_gemm_blockscaled_ws_bytes(uint32_t m, uint32_t n, uint32_t k);
+
+/*
+ * int8_gemm_blockscaled with a caller workspace, for grids too small to fill
+ * the GPU: m > 32 rows in fewer 64 x 64 output tiles than compute units with
+ * k >= 8192 (e.g. m = 48..192 at n = 4096, k = 14336), where it measured
+ * faster than the paths without workspace.  Each tile's K range is cut into
+ * slices of whole 128-element
+ * stages, one workgroup per (tile, slice), each writing its FP32 tile to the
+ * workspace; a second launch adds the slices in slice order and rounds to
+ * BF16.  Same step as the GEMM launch of `int8_gemm_faith2_prefill` (page
+ * "metrale_model_layers/layers/ops/gemm_dense_int8.rs"); the FP32 sum per
+ * output is (sum over the slices, in order, of each slice's chain over its
+ * blocks), within the same tolerance as int8_gemm_blockscaled.  Problems
+ * with no split (int8_gemm_blockscaled_ws_bytes == 0) run exactly as
+ * int8_gemm_blockscaled and do not touch the workspace.
+ *   arguments 1-8 as int8_gemm_blockscaled
+ *   workspace        device buffer of workspace_bytes, 16-byte aligned; its
+ *                    contents on entry do not matter, on return they are
+ *                    scratch; it must not alias any other argument, and two
+ *                    calls that may overlap in time must not share it
+ * Errors: as int8_gemm_blockscaled; when a split runs, BSR_ENULL (workspace
+ * NULL), BSR_EALIGN (workspace), BSR_EINVAL (workspace_bytes below
+ * int8_gemm_blockscaled_ws_bytes(m, n, k)).
+ */
+BSR_API int int8_gemm_blockscaled_ws(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
+                                     const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                                     void *workspace, uint64_t workspace_bytes, void *stream);
+
+/*
  * Fused SiLU·mul -> int8 per-32 requant: the quantized input of the down
  * projection, straight from the gate and up halves of a gate+up output (the
  * SiLU-product quantizer `W8a8Kernels::quant_silu` of page

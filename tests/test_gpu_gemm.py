@@ -369,3 +369,57 @@ def test_scales_at_4_byte_alignment(m, k, path):
     assert sa.data_ptr() % 16 == 4 and sw.data_ptr() % 16 == 4
     out = host(gpu_gemm(da, dw, sa, sw, path=path))
     assert np.array_equal(out, ref)
+
+
+# Grids of fewer 64 x 64 tiles than CUs split K across workgroups when given a
+# workspace (m > 32, K >= 8192): m = 33..192 at n = 4096 and 14336, ragged m,
+# n and K (65 x 130 x 8992: 71 stages, the last one a single block, in 15
+# slices of 5 -- the last slice one partial stage), two slices (48 x 14336,
+# 192 x 4096) and sixteen (129 x 300).
+@pytest.mark.parametrize("m,n,k", [(33, 4096, 14336), (64, 4096, 14336), (65, 130, 8992), (100, 200, 8192),
+                                   (48, 14336, 8192), (129, 300, 8192), (192, 4096, 14336)])
+def test_gemm_split_k_parity(m, n, k):
+    say(f"split-K gemm m={m} n={n} k={k}")
+    need = bsr.int8_gemm_blockscaled_ws_bytes(m, n, k)
+    assert 0 < need <= 8 << 20
+    a, w, a_s, w_s = _rand_operands(900 + m + n, m, n, k, zero_frac=0.03)
+    y, t = oracle.gemm_ref(a, w, a_s, w_s)
+    da, dw, das, dws = to_dev(a), to_dev(w), to_dev(a_s), to_dev(w_s)
+    # the workspace's contents on entry do not matter: NaN-filled, then reused as left
+    ws = torch.full((need // 4 + 64,), float("nan"), dtype=torch.float32, device=DEV)
+    outs = []
+    for _ in range(2):
+        out = canary_out(m, n)
+        bsr.int8_gemm_blockscaled_ws(da, dw, das, dws, out, ws[:need // 4])
+        outs.append(host(out))
+    assert torch.isnan(ws[need // 4:]).all(), "stores past the workspace size"
+    _check(f"split-K {m}x{n}x{k}", outs[0], y, t, k)
+    assert np.array_equal(outs[0], outs[1]), "the split is deterministic"
+
+
+def test_gemm_split_k_errors_and_no_split():
+    m, n, k = 64, 4096, 8192
+    need = bsr.int8_gemm_blockscaled_ws_bytes(m, n, k)
+    assert need > 0
+    a, w, a_s, w_s = _rand_operands(31, m, n, k)
+    da, dw, das, dws = to_dev(a), to_dev(w), to_dev(a_s), to_dev(w_s)
+    out = canary_out(m, n)
+    small = torch.zeros(need // 4 - 4, dtype=torch.float32, device=DEV)
+    with pytest.raises(bsr.BsrError) as e:
+        bsr.int8_gemm_blockscaled_ws(da, dw, das, dws, out, small)
+    assert e.value.status == bsr.BSR_EINVAL
+    with pytest.raises(bsr.BsrError) as e:
+        bsr.int8_gemm_blockscaled_ws(da, dw, das, dws, out, None)
+    assert e.value.status == bsr.BSR_ENULL
+    torch.cuda.synchronize()
+    assert np.all(host(out) == CANARY), "an error launches nothing"
+    # a problem with no split ignores the workspace and equals int8_gemm_blockscaled bit for bit
+    m2, n2, k2 = 1024, 2048, 1024
+    assert bsr.int8_gemm_blockscaled_ws_bytes(m2, n2, k2) == 0
+    a, w, a_s, w_s = _rand_operands(32, m2, n2, k2)
+    da, dw, das, dws = to_dev(a), to_dev(w), to_dev(a_s), to_dev(w_s)
+    ref = canary_out(m2, n2)
+    bsr.int8_gemm_blockscaled(da, dw, das, dws, ref)
+    got = canary_out(m2, n2)
+    bsr.int8_gemm_blockscaled_ws(da, dw, das, dws, got, None)
+    assert np.array_equal(host(got), host(ref))

@@ -28,3 +28,14 @@ def test_w4a16_register_decode_plan_fits_lds(tmp_path):
     assert rc == 0, out
     assert out.startswith("ok ")
     assert int(out.split()[1]) > 100000
+
+
+def test_gemm_split_plan(tmp_path):
+    """The K-split plan covers K with non-empty slices of whole stages, keeps the
+    grid within two workgroups per CU and the workspace within its 8 MiB bound
+    (which sizes the allocation-free entry point's static scratch)."""
+    rc, out = _run_checker("split_plan_check", tmp_path)
+    assert rc == 0, out
+    assert out.startswith("ok ")
+    cases, split = map(int, out.split()[1:])
+    assert split > 1000 and cases > split
