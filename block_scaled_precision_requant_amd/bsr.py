@@ -31,6 +31,7 @@ SIGNATURES = {
     "int8_gemm_blockscaled_agroup": (_int, [_vp, _vp, _vp, _u32, _vp, _vp, _u32, _u32, _u32, _vp, _int]),
     "int8_gemm_blockscaled_ws_bytes": (ctypes.c_uint64, [_u32, _u32, _u32]),
     "int8_gemm_blockscaled_ws": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u32, _u32, _vp, ctypes.c_uint64, _vp]),
+    "int8_gemm_blockscaled_noalloc": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u32, _u32, _vp]),
     "bsr_status_string": (ctypes.c_char_p, [_int]),
 }
 
@@ -213,6 +214,21 @@ def int8_gemm_blockscaled_ws(a_i8, w_i8, a_scale, w_scale, out, workspace, strea
     st = lib().int8_gemm_blockscaled_ws(_ptr(a_i8), _ptr(w_i8), _ptr(a_scale), _ptr(w_scale), _ptr(out), m, n, k,
                                         _ptr(workspace), ws_bytes, _stream(stream, out))
     _done(st, "int8_gemm_blockscaled_ws")
+
+
+def int8_gemm_blockscaled_noalloc(a_i8, w_i8, a_scale, w_scale, out, stream=None):
+    """int8_gemm_blockscaled_ws with the library's static per-GPU scratch as the
+    workspace: allocates nothing; calls that overlap in time on one GPU race."""
+    m, k = a_i8.shape
+    n = w_i8.shape[0]
+    _shape(a_i8, (m, k), "a_i8", BYTES)
+    _shape(w_i8, (n, k), "w_i8", BYTES)
+    _shape(a_scale, (m, k // 32), "a_scale", F32)
+    _shape(w_scale, (n, k // 32), "w_scale", F32)
+    _shape(out, (m, n), "out", BF16)
+    st = lib().int8_gemm_blockscaled_noalloc(_ptr(a_i8), _ptr(w_i8), _ptr(a_scale), _ptr(w_scale), _ptr(out),
+                                             m, n, k, _stream(stream, out))
+    _done(st, "int8_gemm_blockscaled_noalloc")
 
 
 FMT_INT8, FMT_E4M3 = 0, 1

@@ -29,6 +29,27 @@ int check_device() {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Scratch of the allocation-free GEMM entry point: the K-split workspace of
+// int8_gemm_blockscaled_noalloc, one copy per GPU, held until the process
+// ends.  Its size is the largest workspace a split plan asks for.  Host code
+// never uses the symbol itself (that is a host-side stand-in, not a device
+// address): scratch_ptr() looks up, once per device, the address of that
+// device's copy.
+static __device__ __align__(256) float scratch[bsr::kSplitMaxBytes / sizeof(float)];
+std::atomic<void *> g_scratch[kMaxDevices];
+
+// The current device's scratch address (nullptr if the lookup failed).
+void *scratch_ptr() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch[dev].store(p, std::memory_order_release);  // the same value if two threads race here
+    }
+    return p;
+}
+
 bool k_ok(uint32_t k) { return k != 0 && k % 32 == 0; }
 
 // Rows the GEMV takes: one 16-row tile at any K, up to four when K suits the
@@ -167,6 +188,22 @@ int int8_gemm_blockscaled_ws(const int8_t *a_i8, const int8_t *w_i8, const float
     if (int st = check_device()) return st;
     return launched(bsr::launch_gemm_split(a_i8, w_i8, a_scale, w_scale, out, m, n, k,
                                            static_cast<float *>(workspace), plan, static_cast<hipStream_t>(stream)));
+}
+
+int int8_gemm_blockscaled_noalloc(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
+                                  const float *w_scale, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                                  void *stream) {
+    if (int st = gemm_args_check(a_i8, w_i8, a_scale, w_scale, out, m, n, k, BSR_PATH_AUTO)) return st;
+    if (m == 0 || n == 0) return BSR_OK;
+    const bsr::SplitPlan plan = bsr::gemm_split_plan(m, n, k);
+    if (plan.slices == 0)
+        return gemm_launch(a_i8, w_i8, a_scale, k / 32, 0, w_scale, out, m, n, k, stream, BSR_PATH_AUTO);
+    if (plan.bytes > sizeof(scratch)) return BSR_EINVAL;  // beyond the scratch (no plan asks for more)
+    if (int st = check_device()) return st;
+    void *ws = scratch_ptr();
+    if (ws == nullptr) return BSR_EDEVICE;
+    return launched(bsr::launch_gemm_split(a_i8, w_i8, a_scale, w_scale, out, m, n, k, static_cast<float *>(ws),
+                                           plan, static_cast<hipStream_t>(stream)));
 }
 
 int int8_gemm_blockscaled_agroup(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,

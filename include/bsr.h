@@ -182,6 +182,25 @@ BSR_API int int8_gemm_blockscaled_ws(const int8_t *a_i8, const int8_t *w_i8, con
                                      void *workspace, uint64_t workspace_bytes, void *stream);
 
 /*
+ * int8_gemm_blockscaled_ws for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the K-split workspace is the library's own static device array
+ * of 8 MiB per GPU (the most any split plan asks for), held until the process
+ * ends; the call allocates nothing.  Same arguments as int8_gemm_blockscaled
+ * and the same results as int8_gemm_blockscaled_ws, bit for bit.
+ * Every call on one GPU shares that GPU's array: calls that may overlap in
+ * time on one GPU (different streams, or several host threads) race and give
+ * undefined results; calls ordered on one stream do not.  Nothing in the
+ * array must start at zero (each call overwrites what it reads).
+ * Errors: as int8_gemm_blockscaled; BSR_EINVAL if a split would need more
+ * than the 8 MiB array (no problem size does); BSR_EDEVICE if the array's
+ * device address cannot be obtained.
+ */
+BSR_API int int8_gemm_blockscaled_noalloc(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
+                                          const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
+                                          uint32_t k, void *stream);
+
+/*
  * Fused SiLU·mul -> int8 per-32 requant: the quantized input of the down
  * projection, straight from the gate and up halves of a gate+up output (the
  * SiLU-product quantizer `W8a8Kernels::quant_silu` of page
