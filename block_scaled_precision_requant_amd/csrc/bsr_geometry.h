@@ -22,7 +22,7 @@ constexpr int kRqaUnroll = 2;        // chunks per lane, loads issued together
 // Weight requant: one lane per 32-element block (16 packed bytes in,
 // 32 int8 out), 256 lanes per workgroup.
 constexpr int kRqwThreads = 256;
-constexpr int kRqwUnroll = 2;        // blocks per lane, loads issued together
+constexpr int kRqwUnroll = 1;        // blocks per lane (one: stores staged through LDS per wave)
 constexpr int kSiluMinPasses = 8;    // fewest passes per workgroup for the SiLU table kernel
 constexpr int kSiluThreads = 512;    // lanes per workgroup of the SiLU table kernel
 

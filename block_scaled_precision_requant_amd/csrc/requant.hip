@@ -566,7 +566,9 @@ __device__ __forceinline__ void requant_w_block(uint4 p, uint32_t sc, float scal
     s_out = s;
 }
 
-// Each lane handles U blocks kRqwThreads apart, all loads issued first.
+// Each lane handles U blocks kRqwThreads apart, all loads issued first.  The
+// 64 consecutive blocks of a wave (2 KB of codes) go out through LDS, so every
+// store instruction writes 1 KB of consecutive bytes.
 template <int U>
 __global__ __launch_bounds__(kRqwThreads) void requant_w_kernel(const uint4 *__restrict__ packed,
                                                                 const uint16_t *__restrict__ e4m3,
@@ -574,6 +576,9 @@ __global__ __launch_bounds__(kRqwThreads) void requant_w_kernel(const uint4 *__r
                                                                 uint4 *__restrict__ q,
                                                                 float *__restrict__ scale,
                                                                 uint64_t nblocks) {
+    __shared__ uint4 stage[kRqwThreads * 2];
+    const int lane = threadIdx.x & 63;
+    uint4 *wst = stage + (threadIdx.x & ~63) * 2;  // this wave's 128 16-byte slots
     const uint64_t base = (uint64_t)blockIdx.x * kRqwThreads * U + threadIdx.x;
     uint4 p[U];
     uint32_t sc[U];
@@ -586,14 +591,18 @@ __global__ __launch_bounds__(kRqwThreads) void requant_w_kernel(const uint4 *__r
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint64_t b = base + (uint64_t)u * kRqwThreads;
+        const uint64_t b0 = b - lane;  // the wave's first block
         uint4 lo, hi;
         float s;
         requant_w_block(p[u], sc[u], scale2, lo, hi, s);
-        if (b < nblocks) {
-            q[2 * b] = lo;
-            q[2 * b + 1] = hi;
-            scale[b] = s;
-        }
+        if (b < nblocks) scale[b] = s;
+        wst[2 * lane] = lo;
+        wst[2 * lane + 1] = hi;
+        __builtin_amdgcn_wave_barrier();
+        const uint4 v0 = wst[lane], v1 = wst[64 + lane];
+        if (b0 + lane / 2 < nblocks) q[2 * b0 + lane] = v0;
+        if (b0 + 32 + lane / 2 < nblocks) q[2 * b0 + 64 + lane] = v1;
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
