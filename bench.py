@@ -46,6 +46,8 @@ PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA
 PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12   # non-packed FP32 VALU lane operations per second (T)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+GEMM_SOURCES = ["gemm.hip", "bsr_internal.h", "bsr_geometry.h"]
+RQ_SOURCES = ["requant.hip", "bsr_internal.h", "bsr_geometry.h"]
 
 
 def _args():
@@ -56,7 +58,7 @@ def _args():
     p.add_argument("--decode-iters", type=int, default=100)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
-    p.add_argument("--only", choices=["all", "prefill", "large", "decode", "silu", "layouts", "copy"],
+    p.add_argument("--only", choices=["all", "prefill", "large", "split", "decode", "silu", "layouts", "copy"],
                    default="all",
                    help="large: the headline workload alone; prefill: it and the other prefill workloads; "
                         "copy: a plain 256 MiB device copy, the known-size reference for HBM byte counters")
@@ -251,10 +253,13 @@ def main():
         b_ag = burst(pair, reps)
         return {
             "requant_w_nvfp4_int8": dict(one_time=True, us_burst=b_w * 1e6, mb=bytes_w / 1e6,
+                                         hbm_bytes_counters=_traffic(f"requant_w_kernel|{proj.name}", RQ_SOURCES),
                                          gbs=bytes_w / b_w / 1e9, frac_hbm=bytes_w / b_w / 1e9 / PEAK_HBM_GBS),
             "requant_a_int8": dict(us_burst=b_a * 1e6, mb=bytes_a / 1e6, gbs=bytes_a / b_a / 1e9,
+                                   hbm_bytes_counters=_traffic(f"requant_a_kernel|{proj.name}", RQ_SOURCES),
                                    frac_hbm=bytes_a / b_a / 1e9 / PEAK_HBM_GBS),
             "int8_gemm_blockscaled": dict(us_burst=b_g * 1e6, tops=ops / b_g / 1e12,
+                                          hbm_bytes_counters=_traffic(f"gemm_kernel|{proj.name}", GEMM_SOURCES),
                                           frac_int8=ops / b_g / 1e12 / PEAK_INT8_TOPS),
             "requant_a_plus_gemm": dict(us_burst=b_ag * 1e6, tops=ops / b_ag / 1e12,
                                         frac_int8=ops / b_ag / 1e12 / PEAK_INT8_TOPS),
@@ -358,6 +363,45 @@ def main():
             del sets, ow_o, osw_o
             torch.cuda.empty_cache()
         rec["other_prefill"] = others
+
+    # ------------------------------------------------------------ K split across workgroups
+    # The rows between decode and prefill at the down projection's width (n = 4096,
+    # k = 14336): the default path (no workspace) against the K split into a caller
+    # workspace and through the allocation-free entry point's static scratch.
+    if args.only in ("all", "split"):
+        sp = {}
+        dproj = [q for q in inputs.workload("decode").projections if q.name == "decode_m8_n4096_k14336"][0]
+        wp, we = dproj.weight()
+        n, k = dproj.n, dproj.k
+        w_i8 = torch.empty((n, k), dtype=torch.int8, device=dev)
+        w_s = torch.empty((n, k // 32), dtype=torch.float32, device=dev)
+        bsr.requant_w_nvfp4_int8(dev_t(wp), dev_t(we), float(dproj.scale2), w_i8, w_s)
+        ncopy = max(2, int(np.ceil(2 ** 30 / (n * k * 1.125))))
+        copies = [(w_i8.clone(), w_s.clone()) for _ in range(ncopy)]
+        rng_sp = np.random.default_rng(5)
+        for m in (17, 32, 64, 128, 192):
+            a_bits = inputs.bf16_normal(rng_sp, m, k)
+            a_i8 = torch.empty((m, k), dtype=torch.int8, device=dev)
+            a_s = torch.empty((m, k // 32), dtype=torch.float32, device=dev)
+            bsr.requant_a_int8(dev_t(a_bits.view(np.int16)), a_i8, a_s)
+            out = torch.empty((m, n), dtype=torch.int16, device=dev)
+            need = bsr.int8_gemm_blockscaled_ws_bytes(m, n, k)
+            ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev) if need else None
+            t_def = burst(lambda i: bsr.int8_gemm_blockscaled(a_i8, copies[i % ncopy][0], a_s, copies[i % ncopy][1],
+                                                              out, stream=stream), args.decode_iters)
+            t_ws = burst(lambda i: bsr.int8_gemm_blockscaled_ws(a_i8, copies[i % ncopy][0], a_s, copies[i % ncopy][1],
+                                                                out, ws, stream=stream), args.decode_iters)
+            t_na = burst(lambda i: bsr.int8_gemm_blockscaled_noalloc(a_i8, copies[i % ncopy][0], a_s,
+                                                                     copies[i % ncopy][1], out, stream=stream),
+                         args.decode_iters)
+            alg = n * k * 1.125 + m * k * 1.125 + 2 * m * n
+            sp[f"m{m}_n{n}_k{k}"] = dict(workspace_bytes=need, default_us_burst=t_def * 1e6,
+                                         ws_us_burst=t_ws * 1e6, noalloc_us_burst=t_na * 1e6,
+                                         tops_best=2.0 * m * n * k / min(t_def, t_ws) / 1e12,
+                                         gbs_best=alg / min(t_def, t_ws) / 1e9)
+        del copies
+        torch.cuda.empty_cache()
+        rec["split"] = sp
 
     # ------------------------------------------------------------ decode
     if args.only in ("all", "decode"):
@@ -603,8 +647,7 @@ def main():
         g = head["kernels"]["int8_gemm_blockscaled"]
         line["roofline"] = {"bound": "mfma", "achieved": g["tops_in_step"], "peak": PEAK_INT8_TOPS,
                             "unit": "TOPS", "frac": g["tops_in_step"] / PEAK_INT8_TOPS,
-                            "traffic": _traffic("gemm_kernel|large", ["gemm.hip", "bsr_internal.h",
-                                                                      "bsr_geometry.h"]),
+                            "traffic": _traffic("gemm_kernel|large", GEMM_SOURCES),
                             "kernel": "gemm_kernel (int8_gemm_blockscaled, m > 16), large prefill"}
         # The same kernel against the vector ALU, which bounds it: the exact
         # per-block FP32 rescale is one int32 -> FP32 conversion and one FMA per
@@ -622,6 +665,8 @@ def main():
         line["other_prefill"] = rec["other_prefill"]
     if cpu:
         line["cpu_baseline"] = cpu
+    if "split" in rec:
+        line["split_k"] = rec["split"]
     if "decode" in rec:
         line["decode"] = rec["decode"]
     if "silu" in rec:
