@@ -13,9 +13,8 @@ block terms taken in any order (one rounding for the scale product, one for the
 product with P, K/32 - 1 for the additions), plus the final BF16 rounding.  It
 only matters under cancellation, where |y| is far below T.
 
-The W4A16 decode GEMV sums K exact per-element terms instead of K/32 block
-terms, adds up to 16 per-wave partial sums and rounds once for scale_2: its
-bound takes `terms` = K + 16 in place of K/32 (T = sum of |x * w|).
+The W4A16 decode GEMV (T = sum of |x * w| over k) takes `terms` from
+w4a16_terms(K): its two kernels sum differently.
 """
 from dataclasses import dataclass
 
@@ -53,6 +52,21 @@ class CheckResult:
         return (f"{self.count} outputs, {self.failures} failures, {self.needed_ii} passed only by the "
                 f"FP32 sum bound, max rel err {self.max_rel_err:.3e}, max ulp err {self.max_ulp_err:.2f}"
                 + (f", first failure at {self.first_failure}" if self.failures else ""))
+
+
+def w4a16_terms(k):
+    """FP32 sum terms of the W4A16 GEMV's first-order error bound.
+
+    K a multiple of 256 (streamed kernel): per 16-element scale block the 16
+    exact products x * e2m1 are summed in FP32 in one matrix-core operation
+    (at most 15 roundings, each bounded by the block's magnitude sum), the block
+    sum is scaled by its E4M3 scale and added to the wave's accumulator (one
+    rounding per block: K/16 over the row), up to 16 wave partials are added
+    (15) and scale_2 multiplies once (1): K/16 + 31.
+    Other K (register-decode kernel): the exact products x * (e2m1 * s16) are
+    accumulated in FP32 inside the matrix-core operations over the whole K
+    range of a wave, then the wave partials and scale_2: K + 16."""
+    return k / 16 + 31 if k % 256 == 0 else k + 16
 
 
 def check_bf16(out_bits, y64, t, k, terms=None) -> CheckResult:

@@ -75,3 +75,23 @@ def test_cancellation_uses_sum_bound():
     res = check_bf16(out, y, t, 4096)
     assert res.ok and res.needed_ii == 1
     assert not check_bf16(_to_bf16_bits(y * 1.5), np.array([[1e-6]]), np.array([[1e-5]]), 4096).ok
+
+
+def test_w4a16_bound_per_kernel():
+    """The streamed W4A16 kernel (K % 256 == 0) gets the bound of K/16 block terms plus
+    the in-block, wave and scale_2 roundings; the register-decode kernel keeps K + 16."""
+    from oracle.compare import w4a16_terms
+    assert w4a16_terms(14336) == 14336 / 16 + 31
+    assert w4a16_terms(4096) == 4096 / 16 + 31
+    assert w4a16_terms(4128) == 4128 + 16
+    assert w4a16_terms(96) == 96 + 16
+    # an error of half the streamed bound passes, twice it fails (no cancellation help:
+    # y = 0, T large)
+    import numpy as np
+    from oracle.compare import check_bf16
+    k, t = 4096, np.array([[2.0 ** 20]])
+    b = (w4a16_terms(k) + 2) * 2.0 ** -24 * t[0, 0]
+    f32 = lambda v: np.array([[v]], np.float32).view(np.uint32) >> 16
+    ok = check_bf16(f32(0.5 * b).astype(np.uint16), np.zeros((1, 1)), t, k, terms=w4a16_terms(k))
+    bad = check_bf16(f32(2.0 * b).astype(np.uint16), np.zeros((1, 1)), t, k, terms=w4a16_terms(k))
+    assert ok.ok and not bad.ok
