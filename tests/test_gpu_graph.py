@@ -69,3 +69,52 @@ def test_prefill_and_decode_replay_in_graph():
         for i, (g, e) in enumerate(zip(got, want)):
             assert torch.equal(g.view(torch.int8), e.view(torch.int8)), f"replay {rep}, tensor {i}"
         say(f"graph replay {rep}: prefill, GEMV and W4A16 outputs equal the eager launches")
+
+
+def test_split_k_and_noalloc_replay_in_graph():
+    """The K-split GEMM through a caller workspace and through the allocation-free
+    entry point's static scratch, captured in one graph (the no-alloc call is the
+    one callers under capture use): four replays on new activations, each equal to
+    eager launches of the same calls, bit for bit."""
+    rng = np.random.default_rng(92)
+    m, n, k = 64, 1024, 8192
+    need = bsr.int8_gemm_blockscaled_ws_bytes(m, n, k)
+    assert need > 0
+    packed, e4m3 = inputs.nvfp4_weight(rng, n, k, -4, 2)
+    w_i8, w_s = gpu_requant_w(packed, e4m3, inputs.SCALE2_1_448)
+    a = _bf16(rng, m, k)
+    a_i8 = torch.empty((m, k), dtype=torch.int8, device=DEV)
+    a_s = torch.empty((m, k // 32), dtype=torch.float32, device=DEV)
+    ws = torch.empty(need // 4, dtype=torch.float32, device=DEV)
+    out_ws = torch.empty((m, n), dtype=torch.int16, device=DEV)
+    out_na = torch.empty((m, n), dtype=torch.int16, device=DEV)
+
+    def step():
+        bsr.requant_a_int8(a, a_i8, a_s)
+        bsr.int8_gemm_blockscaled_ws(a_i8, w_i8, a_s, w_s, out_ws, ws)
+        bsr.int8_gemm_blockscaled_noalloc(a_i8, w_i8, a_s, w_s, out_na)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()   # first calls look up the device check and the scratch address
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+
+    for rep in range(4):
+        a.copy_(_bf16(rng, m, k))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (out_ws.clone(), out_na.clone())
+        out_ws.zero_()
+        out_na.zero_()
+        ws.fill_(float("nan"))
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], out_ws) and torch.equal(got[1], out_na), f"replay {rep}"
+        assert torch.equal(out_ws, out_na)
+        say(f"graph replay {rep}: split-K GEMM (workspace and static scratch) equals the eager launches")
