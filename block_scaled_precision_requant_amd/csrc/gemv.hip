@@ -803,6 +803,208 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void gemv_stream_kernel(
     }
 }
 
+// Path-invariant GEMV for grids of at most one workgroup per CU (K a
+// multiple of 256): each output's FP32 chain stays on one lane of a chain
+// wave, the work that feeds the chains is spread over PW producer waves.  A
+// round covers PW * G consecutive chunks of 8 blocks; producer p takes
+// chunks g * PW + p of it (g < G), streams them through its own LDS ring as
+// the streamed GEMV does, takes one v_mfma_i32_16x16x32_i8 per block, and
+// writes P (converted to float) of its live outputs and the chunk's scales
+// into the chunk's slot of an exchange buffer.  The CW chain waves then run,
+// for every block in increasing order, acc = fma(P_b, a_s * w_s, acc) with
+// the scale product rounded once to binary32 -- the GEMM's chain, so the
+// bits equal the GEMM's -- one output per lane (16 * ROWS outputs over 64
+// CW lanes).  In round r the producers fill exchange buffer r % 2 while the
+// chain waves read buffer (r - 1) % 2; a barrier ends each round.
+//
+// Exchange slot of a chunk: P of the F = 16 ROWS live outputs as [F][8
+// blocks], then the chunk's scales as the ring holds them: [16 weight rows
+// + ROWS activation rows][8 blocks].  Output f is row 4 q + r, column c of
+// the tile for f = r * 16 QG + 16 q + c (QG live 4-row groups; the MFMA lane
+// 16 q + c holds rows 4 q .. 4 q + 3 of column c).
+template <int ROWS>
+struct RelayGeo {
+    static constexpr int kQG = (ROWS + 3) / 4;  // live 4-row groups: lanes 0 .. 16 kQG - 1
+    static constexpr int kRP = ROWS < 4 ? ROWS : 4;  // live rows of such a lane
+    static constexpr int kF = 16 * kQG * kRP;        // live outputs (16 ROWS)
+    static constexpr int kCW = (kF + 63) / 64;       // chain waves
+    static constexpr int kSFloats = (kGemvCols + ROWS) * kStreamChunkBlocks;
+    static constexpr int kChunkFloats = kF * kStreamChunkBlocks + kSFloats;
+};
+
+template <int ROWS, int PW, int RING, int G, bool AGROUP>
+__global__ __launch_bounds__((PW + RelayGeo<ROWS>::kCW) * 64) void gemv_chain_relay_kernel(
+    const int8_t *__restrict__ a, const int8_t *w, const float *__restrict__ a_s,
+    const float *__restrict__ w_s, uint16_t *__restrict__ out, uint32_t m, uint32_t n, uint32_t k,
+    uint32_t a_ld, uint32_t a_shift) {
+    using Buf = StreamBuf<ROWS>;
+    using Copies = StreamCopies<ROWS, AGROUP>;
+    using RG = RelayGeo<ROWS>;
+    typedef float v4f_ __attribute__((ext_vector_type(4)));
+    constexpr int NC = Copies::kTotal;
+    constexpr int F = RG::kF;
+    constexpr int CB = kStreamChunkBlocks;
+    constexpr uint32_t kSlots = PW * G;  // chunks per round
+    static_assert(NC * (RING - 1) < 64, "the copies in flight fit the vmcnt range");
+    static_assert(ROWS <= kGemvMaxRows && (ROWS & (ROWS - 1)) == 0, "1, 2, 4, 8 or 16 rows");
+    static_assert(CB == 8, "two 16-byte LDS accesses per output and chunk");
+    static_assert(sizeof(Buf::s) == RG::kSFloats * sizeof(float) && RG::kSFloats <= 64 * 4,
+                  "one 16-byte copy per lane moves a chunk's scales");
+    extern __shared__ __attribute__((aligned(1024))) int8_t smem[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int q = lane >> 4;
+    const uint32_t c16 = lane & 15;
+    const uint32_t n0 = blockIdx.x * kGemvCols;
+    const uint32_t nb = k / 32;                          // a multiple of 8
+    const uint32_t nchunks = nb / CB;
+    const uint32_t rounds = (nchunks + kSlots - 1) / kSlots;
+    float *xch = reinterpret_cast<float *>(smem);        // [2][kSlots][chunk floats]
+    Buf *ring = reinterpret_cast<Buf *>(smem + 2 * kSlots * RG::kChunkFloats * sizeof(float));
+
+    if (wave < RG::kCW) {
+        // a chain wave: output f = 64 wave + lane, blocks in increasing order
+        const uint32_t f = 64 * wave + lane;
+        const uint32_t g = f % (16 * RG::kQG);
+        const uint32_t row = 4 * (g / 16) + f / (16 * RG::kQG), col = g % 16;
+        float acc = 0.0f;
+        auto chain = [&](const float *xc) {  // one chunk's 8 blocks
+            const float *pe = xc + f * CB;
+            const float *we = xc + F * CB + col * CB;
+            const float *ae = xc + F * CB + (kGemvCols + row) * CB;
+            const v4f_ p0 = *reinterpret_cast<const v4f_ *>(pe), p1 = *reinterpret_cast<const v4f_ *>(pe + 4);
+            const v4f_ w0 = *reinterpret_cast<const v4f_ *>(we), w1 = *reinterpret_cast<const v4f_ *>(we + 4);
+            const v4f_ a0 = *reinterpret_cast<const v4f_ *>(ae), a1 = *reinterpret_cast<const v4f_ *>(ae + 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc = fmaf(p0[j], a0[j] * w0[j], acc);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc = fmaf(p1[j], a1[j] * w1[j], acc);
+        };
+        for (uint32_t r = 0; r <= rounds; ++r) {
+            if (r > 0 && f < (uint32_t)F) {
+                const float *xb = xch + ((r - 1) & 1) * kSlots * RG::kChunkFloats;
+                const uint32_t live = min(kSlots, nchunks - (r - 1) * kSlots);
+                if (live == kSlots) {
+#pragma unroll
+                    for (uint32_t c = 0; c < kSlots; ++c) chain(xb + c * RG::kChunkFloats);
+                } else {
+                    for (uint32_t c = 0; c < live; ++c) chain(xb + c * RG::kChunkFloats);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this round's reads are done
+            __syncthreads();
+        }
+        if (f < (uint32_t)F && row < m && n0 + col < n) out[(uint64_t)row * n + n0 + col] = f32_to_bf16_rne(acc);
+        return;
+    }
+
+    // a producer: its i-th chunk is chunk (i / G) kSlots + (i % G) PW + pw,
+    // increasing in i, so the chunks below nchunks are its first `mine`
+    const uint32_t pw = wave - RG::kCW;
+    auto chunk_of = [&](uint32_t i) { return (i / G) * kSlots + (i % G) * PW + pw; };
+    uint32_t mine = 0;
+    if (nchunks > pw) {
+        const uint32_t full = (nchunks - pw) / kSlots, rest = (nchunks - pw) % kSlots;  // rest < kSlots
+        mine = full * G + min((uint32_t)G, (rest + PW - 1) / PW);
+    }
+    Buf *pring = ring + pw * RING;
+    const uint32_t slot = lane & 15;
+    auto issue = [&](int bi, uint32_t i) {
+        Buf &b = pring[bi];
+        const uint32_t kb = chunk_of(i) * CB;
+#pragma unroll
+        for (int t = 0; t < kGemvCols / kStreamRowsPerCopy; ++t) {
+            const uint32_t r = t * kStreamRowsPerCopy + (lane >> 4);
+            const int8_t *src = w + (uint64_t)min(n0 + r, n - 1) * k + kb * 32 + ((slot ^ (r & 15)) << 4);
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(b.w + t * 1024), 16, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < Buf::kARows / kStreamRowsPerCopy; ++t) {
+            const uint32_t r = t * kStreamRowsPerCopy + (lane >> 4);
+            const int8_t *src = a + (uint64_t)min(r, m - 1) * k + kb * 32 + ((slot ^ (r & 15)) << 4);
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(b.a + t * 1024), 16, 0, 0);
+        }
+        constexpr uint32_t s16_rows = AGROUP ? kGemvCols : kGemvCols + ROWS;
+#pragma unroll
+        for (int t = 0; t < Copies::kScale16; ++t) {
+            const uint32_t srow = 32 * t + (lane >> 1);
+            const float *src = srow < (uint32_t)kGemvCols
+                                   ? w_s + (uint64_t)min(n0 + srow, n - 1) * nb
+                                   : a_s + (uint64_t)min(srow - kGemvCols, m - 1) * a_ld;
+            if (srow < s16_rows)
+                __builtin_amdgcn_global_load_lds(src + kb + 4 * (lane & 1), (lds_void *)(&b.s[32 * t][0]), 16, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < Copies::kScale4; ++t) {
+            const uint32_t r = 8 * t + (lane >> 3);
+            if (r < (uint32_t)ROWS)
+                __builtin_amdgcn_global_load_lds(a_s + (uint64_t)min(r, m - 1) * a_ld + ((kb + (lane & 7)) >> a_shift),
+                                                 (lds_void *)(&b.s[kGemvCols + 8 * t][0]), 4, 0, 0);
+        }
+    };
+    const uint32_t arow = min(c16, (uint32_t)ROWS - 1);
+    // one chunk: its block products and its scales into exchange slot xs
+    auto produce = [&](int bi, float *xs) {
+        const Buf &b = pring[bi];
+        if (lane < RG::kSFloats / 4) {
+            const v4f_ sv = reinterpret_cast<const v4f_ *>(&b.s[0][0])[lane];
+            reinterpret_cast<v4f_ *>(xs + F * CB)[lane] = sv;
+        }
+        const int8_t *wr = b.w + c16 * kStreamRowBytes;
+        const int8_t *ar = b.a + arow * kStreamRowBytes;
+        auto off = [&](uint32_t r, int blk) {
+            return ((((uint32_t)(2 * blk) + (q >> 1)) ^ (r & 15)) << 4) + 8 * (q & 1);
+        };
+        const v4i zero4 = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < CB / 4; ++i) {
+            v4i p[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const long wv = *reinterpret_cast<const long *>(wr + off(c16, 4 * i + j));
+                const long av = *reinterpret_cast<const long *>(ar + off(arow, 4 * i + j));
+                p[j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, wv, zero4, 0, 0, 0);
+            }
+            if (q < RG::kQG) {
+#pragma unroll
+                for (int r = 0; r < RG::kRP; ++r) {
+                    const v4f_ pv = {(float)p[0][r], (float)p[1][r], (float)p[2][r], (float)p[3][r]};
+                    *reinterpret_cast<v4f_ *>(xs + (r * 16 * RG::kQG + lane) * CB + 4 * i) = pv;
+                }
+            }
+        }
+    };
+
+#pragma unroll
+    for (int r = 0; r < RING - 1; ++r)
+        if ((uint32_t)r < mine) issue(r, r);
+    for (uint32_t r = 0; r <= rounds; ++r) {
+        float *xb = xch + (r & 1) * kSlots * RG::kChunkFloats;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const uint32_t i = r * G + g;
+            if (i < mine) {
+                // ring buffer (i + RING - 1) % RING held chunk i - 1, whose reads are done
+                if (i + RING - 1 < mine) issue((i + RING - 1) % RING, i + RING - 1);
+                wait_vm_later<NC, RING - 1>(min(mine - 1 - i, (uint32_t)RING - 1));
+                asm volatile("" ::: "memory");
+                produce(i % RING, xb + (g * PW + pw) * RG::kChunkFloats);
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): ring reads and exchange writes are done
+                asm volatile("" ::: "memory");
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// LDS bytes of the relay kernel: the exchange (two buffers of PW G chunks)
+// and the producers' rings.
+template <int ROWS, int PW, int RING, int G>
+constexpr uint32_t relay_lds() {
+    return 2 * PW * G * RelayGeo<ROWS>::kChunkFloats * sizeof(float) + PW * RING * sizeof(StreamBuf<ROWS>);
+}
+
 }  // namespace
 
 namespace {
@@ -831,6 +1033,38 @@ hipError_t launch_chain_stream(const int8_t *a_i8, const int8_t *w_i8, const flo
     return hipGetLastError();
 }
 
+// The relay kernel's producer waves, ring depth and chunks per producer and
+// round per row count: as many producers as LDS holds with RING - 1 chunks
+// in flight each.
+template <int ROWS>
+struct RelayCfg {
+    static constexpr int kPW = ROWS <= 1 ? 6 : ROWS <= 2 ? 8 : ROWS <= 4 ? 7 : 4;
+    static constexpr int kRing = ROWS <= 1 ? 3 : 2;
+    static constexpr int kG = ROWS <= 1 ? 3 : ROWS <= 8 ? 2 : 1;
+};
+template <int ROWS, bool AGROUP>
+hipError_t launch_chain_relay(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
+                              uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
+                              uint32_t k, hipStream_t s) {
+    constexpr int PW = RelayCfg<ROWS>::kPW, RING = RelayCfg<ROWS>::kRing, G = RelayCfg<ROWS>::kG;
+    constexpr uint32_t lds = relay_lds<ROWS, PW, RING, G>();
+    static_assert(lds <= kLdsBytes, "exchange and rings fit in LDS");
+    hipLaunchKernelGGL((gemv_chain_relay_kernel<ROWS, PW, RING, G, AGROUP>), dim3((uint32_t)div_up(n, kGemvCols)),
+                       dim3(64 * (PW + RelayGeo<ROWS>::kCW)), lds, s, a_i8, w_i8, a_scale, w_scale, out, m, n, k, a_ld, a_shift);
+    return hipGetLastError();
+}
+
+template <bool AGROUP>
+hipError_t launch_chain_relay_rows(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
+                                   uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
+                                   uint32_t k, hipStream_t s) {
+    if (m <= 1) return launch_chain_relay<1, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+    if (m <= 2) return launch_chain_relay<2, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+    if (m <= 4) return launch_chain_relay<4, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+    if (m <= 8) return launch_chain_relay<8, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+    return launch_chain_relay<16, AGROUP>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+}
+
 template <bool AGROUP>
 hipError_t launch_chain_stream_rows(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
                                     uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
@@ -850,6 +1084,10 @@ hipError_t launch_gemv_chain(const int8_t *a_i8, const int8_t *w_i8, const float
     if (k % kGemvStreamKAlign == 0 && div_up(n, kGemvCols) > (uint64_t)kGemmCus) {
         if (a_shift) return launch_chain_stream_rows<true>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
         return launch_chain_stream_rows<false>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+    }
+    if (k % kGemvStreamKAlign == 0) {
+        if (a_shift) return launch_chain_relay_rows<true>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
+        return launch_chain_relay_rows<false>(a_i8, w_i8, a_scale, a_ld, a_shift, w_scale, out, m, n, k, s);
     }
     const dim3 grid((uint32_t)div_up(n, kGemvCols)), blk(64);
     const uint32_t nb = k / 32;

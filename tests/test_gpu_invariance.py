@@ -37,7 +37,7 @@ def _operands(seed, m, n, k):
     return a, packed, e4m3
 
 
-@pytest.mark.parametrize("k", [32, 96, 1056, 1152, 4096, 14336])   # 1152: a partial last chunk
+@pytest.mark.parametrize("k", [32, 96, 256, 1056, 1152, 2304, 4096, 14336])  # 1152: a partial last chunk
 @pytest.mark.parametrize("m", [1, 2, 3, 5, 8, 9, 16])
 def test_invariant_gemv_equals_gemm(m, k):
     n = 200
