@@ -125,6 +125,14 @@ __device__ __forceinline__ void wait_vm_later(uint32_t later) {
     }
 }
 
+// Workgroup barrier without the fences of __syncthreads(), whose release
+// side waits for every outstanding vector-memory operation (vmcnt(0)) and
+// so would drain the LDS copies a ring keeps in flight across the barrier.
+// Callers wait for what the barrier publishes: lgkmcnt(0) for their LDS
+// reads and writes, vmcnt for their own copies that the next step reads.
+// The memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // ---------------------------------------------------------------- direct
 
 // Scales of blocks idx..idx+3 of one row: one 16-byte load when every row
@@ -893,7 +901,7 @@ __global__ __launch_bounds__((PW + RelayGeo<ROWS>::kCW) * 64) void gemv_chain_re
                 }
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this round's reads are done
-            __syncthreads();
+            ring_barrier();
         }
         if (f < (uint32_t)F && row < m && n0 + col < n) out[(uint64_t)row * n + n0 + col] = f32_to_bf16_rne(acc);
         return;
@@ -994,7 +1002,7 @@ __global__ __launch_bounds__((PW + RelayGeo<ROWS>::kCW) * 64) void gemv_chain_re
                 asm volatile("" ::: "memory");
             }
         }
-        __syncthreads();
+        ring_barrier();  // the copies of later chunks stay in flight
     }
 }
 
