@@ -413,7 +413,8 @@ __global__ __launch_bounds__(kW4StreamMaxWaves * 64) void w4a16_stream_kernel(
     }
 }
 
-template <int ROWS, int RING = 2>
+constexpr int kW4StreamRing = 2;
+template <int ROWS, int RING = kW4StreamRing>
 hipError_t launch_w4a16_stream(const uint16_t *x, const uint8_t *w_packed, const uint8_t *w_e4m3, float scale2,
                                uint16_t *out, uint32_t m, uint32_t n, uint32_t k, hipStream_t s) {
     constexpr uint32_t ring_bytes = RING * sizeof(W4Buf<ROWS>);
