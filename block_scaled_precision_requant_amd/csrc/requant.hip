@@ -97,7 +97,12 @@ __device__ __forceinline__ uint32_t e4m3_rne(float x) {
     return sign | code;
 }
 
-// E4M3 codes of 8 values of a block with scale s = fl32(amax / 448).
+// E4M3 codes of 8 values of a block with scale s = fl32(amax / 448): the
+// nearest E4M3 value of fl32(v / s), with the IEEE divide.  (A reciprocal
+// fast path as in int8_codes does not pay here: with BF16 values and
+// 448 = 7 * 2^6 many quotients fall exactly on E4M3 midpoints, so nearly
+// every wave would also run the divide for its tied elements -- measured
+// 40 % slower.)
 __device__ __forceinline__ uint2 e4m3_codes(const float (&v)[8], float s) {
     if (s == 0.0f) return make_uint2(0u, 0u);
     uint32_t c[8];
@@ -397,19 +402,35 @@ __global__ __launch_bounds__(kRqaThreads) void quant_group_kernel(const uint4 *_
     }
 }
 
-// One scale per row: one workgroup per row, two passes over the row (the
-// second re-reads it from the caches).
-template <bool E4M3>
+// One scale per row: one workgroup per row.  U > 0: the row's chunks (at
+// most U per lane) stay in registers between the amax and the quantization;
+// U = 0: two passes over the row (the second re-reads it from the caches).
+template <bool E4M3, int U>
 __global__ __launch_bounds__(kRqaThreads) void quant_row_kernel(const uint4 *__restrict__ a,
                                                                 uint2 *__restrict__ q,
                                                                 float *__restrict__ scale, uint32_t kc) {
     __shared__ float wmax[kRqaThreads / 64];
     const uint64_t row0 = (uint64_t)blockIdx.x * kc;
+    uint4 raw[U > 0 ? U : 1];
     float amax = 0.0f;
-    for (uint32_t c = threadIdx.x; c < kc; c += kRqaThreads) {
-        float v[8];
-        bf16_chunk(a[row0 + c], v);
-        amax = fmaxf(amax, local_amax(v));
+    if constexpr (U > 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t c = threadIdx.x + u * kRqaThreads;
+            raw[u] = c < kc ? a[row0 + c] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float v[8];
+            bf16_chunk(raw[u], v);  // +0 past the row's end
+            amax = fmaxf(amax, local_amax(v));
+        }
+    } else {
+        for (uint32_t c = threadIdx.x; c < kc; c += kRqaThreads) {
+            float v[8];
+            bf16_chunk(a[row0 + c], v);
+            amax = fmaxf(amax, local_amax(v));
+        }
     }
     amax = row16_max(amax);
     amax = fmaxf(amax, __shfl_xor(amax, 16));
@@ -419,12 +440,37 @@ __global__ __launch_bounds__(kRqaThreads) void quant_row_kernel(const uint4 *__r
 #pragma unroll
     for (int w = 0; w < kRqaThreads / 64; ++w) amax = fmaxf(amax, wmax[w]);
     const float s = amax / (E4M3 ? 448.0f : 127.0f);
-    for (uint32_t c = threadIdx.x; c < kc; c += kRqaThreads) {
-        float v[8];
-        bf16_chunk(a[row0 + c], v);
-        q[row0 + c] = E4M3 ? e4m3_codes(v, s) : int8_codes(v, s);
+    if constexpr (U > 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t c = threadIdx.x + u * kRqaThreads;
+            if (c < kc) {
+                float v[8];
+                bf16_chunk(raw[u], v);
+                q[row0 + c] = E4M3 ? e4m3_codes(v, s) : int8_codes(v, s);
+            }
+        }
+    } else {
+        for (uint32_t c = threadIdx.x; c < kc; c += kRqaThreads) {
+            float v[8];
+            bf16_chunk(a[row0 + c], v);
+            q[row0 + c] = E4M3 ? e4m3_codes(v, s) : int8_codes(v, s);
+        }
     }
     if (threadIdx.x == 0) scale[blockIdx.x] = s;
+}
+
+// The per-row kernel for kc chunks a row: chunks per lane rounded up to 1,
+// 2, 4 or 8, else two passes.
+template <bool E4M3>
+void launch_quant_row(const uint4 *a, uint2 *q, float *scale, uint32_t m, uint32_t kc, hipStream_t s) {
+    const uint64_t per_lane = div_up(kc, kRqaThreads);
+    const dim3 grid(m), blk(kRqaThreads);
+    if (per_lane <= 1) hipLaunchKernelGGL((quant_row_kernel<E4M3, 1>), grid, blk, 0, s, a, q, scale, kc);
+    else if (per_lane <= 2) hipLaunchKernelGGL((quant_row_kernel<E4M3, 2>), grid, blk, 0, s, a, q, scale, kc);
+    else if (per_lane <= 4) hipLaunchKernelGGL((quant_row_kernel<E4M3, 4>), grid, blk, 0, s, a, q, scale, kc);
+    else if (per_lane <= 8) hipLaunchKernelGGL((quant_row_kernel<E4M3, 8>), grid, blk, 0, s, a, q, scale, kc);
+    else hipLaunchKernelGGL((quant_row_kernel<E4M3, 0>), grid, blk, 0, s, a, q, scale, kc);
 }
 
 // OCP E4M3 code -> binary32.  Its exponent and mantissa bits shifted into a
@@ -646,8 +692,8 @@ hipError_t launch_quant_act(const uint16_t *a_bf16, uint8_t *q, float *scale, ui
     const dim3 blk(kRqaThreads);
     const dim3 grid((uint32_t)div_up(nchunks, (uint64_t)kRqaThreads * kRqaUnroll));
     if (group == 0) {
-        if (e4m3) hipLaunchKernelGGL(quant_row_kernel<true>, dim3(m), blk, 0, s, a, qq, scale, kc);
-        else hipLaunchKernelGGL(quant_row_kernel<false>, dim3(m), blk, 0, s, a, qq, scale, kc);
+        if (e4m3) launch_quant_row<true>(a, qq, scale, m, kc, s);
+        else launch_quant_row<false>(a, qq, scale, m, kc, s);
     } else if (group == 32) {
         if (e4m3) hipLaunchKernelGGL((quant_group_kernel<true, 4, kRqaUnroll>), grid, blk, 0, s, a, qq, scale, nchunks);
         else hipLaunchKernelGGL((quant_group_kernel<false, 4, kRqaUnroll>), grid, blk, 0, s, a, qq, scale, nchunks);

@@ -35,7 +35,11 @@ def _assert_quant_equal(name, a_bits, group, fmt, e4m3):
 
 @pytest.mark.parametrize("group", [32, 128, 0])
 @pytest.mark.parametrize("fmt,e4m3", FORMATS)
-@pytest.mark.parametrize("m,k", [(1, 128), (37, 640), (300, 1024), (64, 14336), (5, 96)])
+# The per-row kernel keeps a row's 8-element chunks in registers, one per lane
+# up to k = 2048, then two (k = 4096), four (8192) or eight (14336) per lane;
+# k = 16640 (more than 2048 chunks) takes its two-pass form.
+@pytest.mark.parametrize("m,k", [(1, 128), (37, 640), (300, 1024), (64, 14336), (5, 96), (2, 4096), (2, 8192),
+                                 (3, 16640)])
 def test_quantize_act_matches_oracle(m, k, group, fmt, e4m3):
     if group == 128 and k % 128:
         pytest.skip("k not a multiple of 128")
