@@ -155,11 +155,44 @@ def default_named():
     return named
 
 
+def decode_named():
+    """The decode launches of `bench.py --only decode`, per case (m rows padded
+    to 1, 2, 4 or 8): the default GEMV, the path-invariant GEMV and the W4A16
+    GEMV, with the launch shapes their plans give at N = 14336, K = 4096 and
+    N = 4096, K = 14336, and their algorithmic bytes per launch."""
+    sys.path.insert(0, ROOT)
+    from block_scaled_precision_requant_amd import inputs
+    relay = {1: ("1, 6, 3, 3", 448), 2: ("2, 8, 2, 2", 576), 4: ("4, 7, 2, 2", 512), 8: ("8, 4, 2, 2", 384)}
+    w4_threads_wide = {1: 512, 2: 512, 4: 256, 8: 192}
+    named = {}
+    for p in inputs.workload("decode").projections:
+        m, n, k = p.m, p.n, p.k
+        rows = 1 if m <= 1 else 2 if m <= 2 else 4 if m <= 4 else 8
+        wide = n > 4096
+        int8_alg = n * k * 9 // 8 + m * k * 9 // 8 + 2 * m * n
+        named[f"gemv|{p.name}"] = dict(
+            kernel=f"gemv_stream_kernel<{rows}, 2, false>", grid=896 * 128 if wide else 256 * 512,
+            workload=f"decode GEMV {m}x{n}x{k}", alg=int8_alg)
+        if wide:
+            named[f"invariant|{p.name}"] = dict(
+                kernel=f"gemv_stream_kernel<{rows}, 4, false>", grid=896 * 64,
+                workload=f"path-invariant GEMV {m}x{n}x{k}", alg=int8_alg)
+        else:
+            tmpl, threads = relay[rows]
+            named[f"invariant|{p.name}"] = dict(
+                kernel=f"gemv_chain_relay_kernel<{tmpl}, false>", grid=256 * threads,
+                workload=f"path-invariant GEMV {m}x{n}x{k}", alg=int8_alg)
+        named[f"w4a16|{p.name}"] = dict(
+            kernel=f"w4a16_stream_kernel<{rows}, 2>", grid=896 * w4_threads_wide[rows] if wide else 256 * 512,
+            workload=f"W4A16 GEMV {m}x{n}x{k}", alg=n * k * 9 // 16 + 2 * m * k + 2 * m * n)
+    return named
+
+
 def cmd_traffic(args):
     fetch, write = _counter(args.fetch, "FETCH_SIZE"), _counter(args.write, "WRITE_SIZE")
     f_kib, f_scale = _copy_scale(args.fetch_copy, "FETCH_SIZE")
     w_kib, w_scale = _copy_scale(args.write_copy, "WRITE_SIZE")
-    named = json.loads(args.named) if args.named else default_named()
+    named = json.loads(args.named) if args.named else decode_named() if args.set == "decode" else default_named()
     out = {}
     rows = []
     for label, spec in named.items():
@@ -234,7 +267,9 @@ def main():
     c = sub.add_parser("traffic")
     for a in ("fetch", "write", "fetch_copy", "write_copy", "out_json", "out_md"):
         c.add_argument(a)
-    c.add_argument("--named", help="JSON {label: {kernel, grid, workload, alg}} (default: the prefill launches)")
+    c.add_argument("--named", help="JSON {label: {kernel, grid, workload, alg}} (default: the --set launches)")
+    c.add_argument("--set", choices=["prefill", "decode"], default="prefill",
+                   help="launches to summarize: the prefill kernels or the decode GEMVs")
     c.add_argument("--command", action="append", required=True)
     s = sub.add_parser("sq")
     s.add_argument("dirs", nargs="+")
