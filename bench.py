@@ -574,6 +574,33 @@ def main():
                                    frac_hbm=2 * src.numel() / t_c / 1e9 / PEAK_HBM_GBS)
         del src, dst
         torch.cuda.empty_cache()
+        # a plain streaming read (read_probe.hip: 16-byte loads in a grid-stride
+        # loop, libbsr_read.so), per launch, at the decode weights' sizes and at
+        # 1 GiB, buffers rotated over >= 1 GiB: what one launch of that many bytes
+        # costs here, launch and ramp included (best of three grid sizes)
+        rlib = ctypes.CDLL(os.path.join(os.path.dirname(bsr.LIB_PATH), "libbsr_read.so"))
+        rlib.read_probe.restype = ctypes.c_int
+        rlib.read_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint32,
+                                    ctypes.c_void_p]
+        sink = torch.empty(4096, dtype=torch.int32, device=dev)
+        reads = {}
+        for label, nbytes in (("33MB", 33_554_432), ("66MB", 67_108_864), ("1GiB", 2 ** 30)):
+            nbuf = max(2, -(-2 ** 30 // nbytes))
+            bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+            best = None
+            for grid in (1024, 2048, 4096):
+                def read(i, grid=grid):
+                    rc = rlib.read_probe(ctypes.c_void_p(bufs[i % nbuf].data_ptr()), nbytes,
+                                         ctypes.c_void_p(sink.data_ptr()), grid, ctypes.c_void_p(stream.cuda_stream))
+                    assert rc == 0
+                t_r = burst(read, 50 if nbytes < 2 ** 30 else 10)
+                if best is None or t_r < best[0]:
+                    best = (t_r, grid)
+            reads[label] = dict(bytes=nbytes, us=best[0] * 1e6, gbs=nbytes / best[0] / 1e9,
+                                frac_hbm=nbytes / best[0] / 1e9 / PEAK_HBM_GBS, grid=best[1])
+            del bufs
+            torch.cuda.empty_cache()
+        rec["read_context"] = reads
 
     # ------------------------------------------------------------ CPU oracle
     # The oracle (as is, OpenMP over rows) on the host threads, on the headline
@@ -675,6 +702,8 @@ def main():
         line["activation_layouts"] = rec["layouts"]
     if "copy_context" in rec:
         line["copy_context"] = rec["copy_context"]
+    if "read_context" in rec:
+        line["read_context"] = rec["read_context"]
     print(json.dumps(line), flush=True)
 
 

@@ -19,6 +19,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsr.so")
 SOURCES = ["requant.hip", "gemm.hip", "gemv.hip", "w4a16.hip", "api.hip"]
+# The streaming-read kernel bench.py reports as bandwidth context: a library of
+# its own, so libbsr.so exports only the entry points include/bsr.h declares.
+READ_LIB = os.path.join(PKG, "libbsr_read.so")
+READ_SOURCE = "read_probe.hip"
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -68,15 +72,23 @@ def _version_script():
 def build(verbose: bool = False, save_temps: bool = False) -> str:
     """Compile every kernel source and link libbsr.so; returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, save_temps), SOURCES))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        objs = list(ex.map(lambda s: _compile(s, save_temps), SOURCES + [READ_SOURCE]))
+    read_obj = objs.pop()
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs,
            f"-Wl,--version-script={_version_script()}", "-o", tmp]
     subprocess.run(cmd, check=True, capture_output=not verbose)
     os.replace(tmp, LIB)
+    tmp = READ_LIB + ".tmp%d" % os.getpid()
+    read_map = os.path.join(BUILD, "libbsr_read.map")
+    with open(read_map, "w") as f:
+        f.write("{\n  global:\n    read_probe;\n  local: *;\n};\n")
+    subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", read_obj,
+                    f"-Wl,--version-script={read_map}", "-o", tmp], check=True, capture_output=not verbose)
+    os.replace(tmp, READ_LIB)
     if verbose:
-        print(LIB)
+        print(LIB, READ_LIB)
     return LIB
 
 

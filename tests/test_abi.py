@@ -198,3 +198,18 @@ def test_gemm_k_limit():
         bsr.BSR_EINVAL
     assert L.int8_gemm_blockscaled(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, k, None) != bsr.BSR_EINVAL
     assert L.int8_gemm_blockscaled(FAKE, FAKE, FAKE, FAKE, FAKE, 17, 8, k - 32, None) != bsr.BSR_EINVAL
+
+
+def test_read_probe_library_exports_one_symbol():
+    """The bandwidth-context read kernel (bench.py) lives in a library of its own
+    that defines read_probe and nothing else; invalid arguments are refused
+    before any launch."""
+    path = os.path.join(os.path.dirname(bsr.LIB_PATH), "libbsr_read.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    assert {line.split()[-1] for line in out.splitlines() if line.strip()} == {"read_probe"}
+    L = ctypes.CDLL(path)
+    L.read_probe.restype = ctypes.c_int
+    L.read_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]
+    assert L.read_probe(None, 16, FAKE, 1, None) == 1           # null buffer
+    assert L.read_probe(FAKE, 15, FAKE, 1, None) == 1           # not whole 16-byte words
+    assert L.read_probe(FAKE, 16, FAKE, 0, None) == 1           # empty grid
