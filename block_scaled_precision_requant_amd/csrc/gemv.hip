@@ -30,12 +30,15 @@
 //    per wave step;
 //  * direct: every operand comes from global memory.  Used when the staged
 //    copies do not fit in LDS or K is not a multiple of 128;
-//  * chain (the path-invariant GEMV): one wave per workgroup runs all of K in
-//    block order, so each output is the same FP32 chain
+//  * chain (the path-invariant GEMV): each output is the same FP32 chain
 //    acc = fma(P_b, fl32(a_s * w_s), acc), b = 0, 1, ..., that the GEMM
-//    evaluates -- its BF16 bits equal the GEMM's.  The streamed form
-//    (K % 128 == 0) brings every operand through an LDS ring and takes K = 32
-//    MFMAs; the register form is the fallback.
+//    evaluates, held on one lane from the first block to the last -- its
+//    BF16 bits equal the GEMM's.  On grids of at most one workgroup per CU
+//    (K % 256 == 0) producer waves stream the chunks and take the block
+//    products, and chain waves run the chains from an LDS exchange (relay);
+//    on wider grids one wave per workgroup walks all of K (the streamed
+//    kernel's loop); other K take the one-wave LDS-ring form (K % 128 == 0)
+//    or the register form.
 #include <type_traits>
 
 #include "bsr_internal.h"
