@@ -356,10 +356,15 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
             const int t = u >> 1, j = u & 1;
             if (u + 1 < kUnits) {
                 const int t1 = (u + 1) >> 1, j1 = (u + 1) & 1;
+                // The wave issuing matrix-core work goes ahead of the other
+                // wave's rescale on the same SIMD, so the matrix core is fed
+                // as soon as its operands are ready.
+                __builtin_amdgcn_s_setprio(1);
                 if (j1 == 0)
                     sc[t1 & 1] = __builtin_amdgcn_mfma_f32_32x32x1f32(asv[t1 / TN], wsv[t1 % TN], zero32, 0, 0, 0);
                 p[(u + 1) & 1] =
                     __builtin_amdgcn_mfma_i32_32x32x32_i8(af[t1 / TN][j1], bf[t1 % TN][j1], zero16, 0, 0, 0);
+                __builtin_amdgcn_s_setprio(0);
             }
             float *ac = acc[t / TN][t % TN];
 #pragma unroll
