@@ -43,7 +43,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "int8 block-scaled GEMM TOPS (prefill) + GEMV HBM GB/s, % of MI355X peak"
 PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA
-PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12   # non-packed FP32 VALU lane operations per second (T)
+PEAK_VALU_TOPS = 157.3 / 2                     # FP32 vector peak 157.3 TFLOP/s as FMA lane operations (T/s)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 GEMM_SOURCES = ["gemm.hip", "bsr_internal.h", "bsr_geometry.h"]
@@ -678,8 +678,10 @@ def main():
                             "kernel": "gemm_kernel (int8_gemm_blockscaled, m > 16), large prefill"}
         # The same kernel against the vector ALU, which bounds it: the exact
         # per-block FP32 rescale is one int32 -> FP32 conversion and one FMA per
-        # output and 32-wide K block; peak = 256 CUs x 4 SIMDs x 16 lanes x
-        # 2.4 GHz non-packed FP32 lane operations.
+        # output and 32-wide K block; peak = the FP32 vector peak, 157.3 TFLOP/s,
+        # counted as FMA lane operations (78.6 T/s).  The SQ counters of this
+        # kernel show wave64 VALU instructions issuing faster than 16 lanes per
+        # cycle, so 16 lanes x 4 SIMDs x 256 CUs x 2.4 GHz is no ceiling.
         alu_ops = 2.0 * M * N * (K // 32)
         alu = alu_ops / (g["us_in_step_mean"] * 1e-6) / 1e12
         line["roofline_alu"] = {"bound": "alu", "achieved": alu, "peak": PEAK_VALU_TOPS,
