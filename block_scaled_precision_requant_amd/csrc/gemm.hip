@@ -17,7 +17,12 @@
 // from global memory into LDS with buffer loads (no registers held while the
 // copy is in flight, and per-lane offsets fixed for the whole K loop) into a
 // ring of RING buffers; the next RING - 1 stages are in flight while the
-// current one is computed, with one barrier per stage.
+// current one is computed, with one barrier per stage.  A copy costs about
+// one cycle of the CU's load path per cache line it touches, whatever its
+// bytes, so the large 128 x 128 shape stages its scales 8 blocks (32 bytes
+// of a row) at a time, every other stage, and spreads the next stage's copies
+// over the units of its first block pair instead of issuing them all after
+// the barrier, where the eight waves of a CU queued behind each other.
 #include "bsr_internal.h"
 
 namespace bsr {
@@ -83,6 +88,24 @@ struct Stage {
     float ws[BN][kGemmStageBlocks];
 };
 
+// The 128 x 128 shape keeps its scales apart from the operand ring: one
+// scale stage covers two operand stages (8 blocks, 32 bytes of every scale
+// row), so a scale copy touches 8 rows' cache lines instead of 16.  Its 8
+// blocks of row r are permuted by scale_swz8(r): 32 consecutive rows read at
+// one block then hit 32 distinct banks (32- or 64-bank LDS).
+template <int BM, int BN>
+struct OpStage {
+    int8_t a[BM * kGemmStageBytes];
+    int8_t w[BN * kGemmStageBytes];
+};
+constexpr int kSc8Blocks = 2 * kGemmStageBlocks;
+template <int BM, int BN>
+struct Sc8Stage {
+    float as[BM][kSc8Blocks];  // [row][block ^ scale_swz8(row)]
+    float ws[BN][kSc8Blocks];
+};
+__device__ __forceinline__ uint32_t scale_swz8(uint32_t r) { return (r >> 2) & 7; }
+
 // Operand staging: buffer loads straight into LDS.  A wave's copy fills LDS
 // in lane order (16 bytes per lane for operand rows, 4 for scales); the lane
 // whose LDS slot is (row, slot) fetches chunk slot ^ chunk_swz(row), and scale
@@ -99,10 +122,12 @@ struct Stage {
 // r reads a_s[r * ld + (b >> shift)]: ld = nb, shift = 0 for a scale per
 // block; a scale per 128 elements has ld = nb / 4, shift = 2, one per row
 // ld = 1, shift = 31.
-template <int BM, int BN, int NWAVES>
+template <int BM, int BN, int NWAVES, bool SC8 = false>
 struct BufStage {
     static constexpr int kSegA = BM / kRowsPerCopy, kSegW = BN / kRowsPerCopy;
-    static constexpr int kSegAs = BM * kGemmStageBlocks / 64, kSegWs = BN * kGemmStageBlocks / 64;
+    // scale copies: 64 lanes = 16 rows x 4 blocks, or 8 rows x 8 blocks (SC8)
+    static constexpr int kScBlocks = SC8 ? kSc8Blocks : kGemmStageBlocks;
+    static constexpr int kSegAs = BM * kScBlocks / 64, kSegWs = BN * kScBlocks / 64;
     static constexpr int kNA = (kSegA + NWAVES - 1) / NWAVES, kNW = (kSegW + NWAVES - 1) / NWAVES;
     static constexpr int kNAs = (kSegAs + NWAVES - 1) / NWAVES, kNWs = (kSegWs + NWAVES - 1) / NWAVES;
     __amdgpu_buffer_rsrc_t ra, rw, ras, rws;
@@ -134,15 +159,40 @@ struct BufStage {
         }
 #pragma unroll
         for (int i = 0; i < kNAs; ++i) {
-            const uint32_t idx = (wave + i * NWAVES) * 64 + lane, row = idx / kGemmStageBlocks;
-            const uint32_t blk = (idx % kGemmStageBlocks) ^ scale_swz(row);
-            oas[i] = row * a_ld * 4 + (shift == 0 ? blk * 4 : 0);
+            const uint32_t idx = (wave + i * NWAVES) * 64 + lane, row = idx / kScBlocks;
+            const uint32_t blk = (idx % kScBlocks) ^ (SC8 ? scale_swz8(row) : scale_swz(row));
+            // a scale per 2^shift blocks; a stage's first block is a multiple of 4
+            oas[i] = row * a_ld * 4 + (shift >= 31 ? 0u : (blk >> shift) * 4);
         }
 #pragma unroll
         for (int i = 0; i < kNWs; ++i) {
-            const uint32_t idx = (wave + i * NWAVES) * 64 + lane, row = idx / kGemmStageBlocks;
-            const uint32_t blk = (idx % kGemmStageBlocks) ^ scale_swz(row);
+            const uint32_t idx = (wave + i * NWAVES) * 64 + lane, row = idx / kScBlocks;
+            const uint32_t blk = (idx % kScBlocks) ^ (SC8 ? scale_swz8(row) : scale_swz(row));
             ows[i] = row * nb * 4 + blk * 4;
+        }
+    }
+
+    // SC8, one copy I (compile-time) of a stage's 12: the 8 operand segments
+    // of the stage from block kb into (sa, sw), then 4 scale copies -- the A
+    // scale rows of the 8 blocks from kbs into sas when !wside, else the W
+    // scale rows into sws (every count divides evenly among the 4 waves).
+    template <int I>
+    __device__ __forceinline__ void issue_one(int8_t *sa, int8_t *sw, float *sas, float *sws, uint32_t kb,
+                                              uint32_t kbs, bool wside, int wave) const {
+        static_assert(SC8 && NWAVES == 4 && kNA == 4 && kNW == 4 && kNAs == 4 && kNWs == 4, "the 128 x 128 shape");
+        if constexpr (I < kNA) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(sa + (wave + I * NWAVES) * 1024), 16, oa[I],
+                                                     kb * 32, 0, 0);
+        } else if constexpr (I < kNA + kNW) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(sw + (wave + (I - kNA) * NWAVES) * 1024), 16,
+                                                     ow[I - kNA], kb * 32, 0, 0);
+        } else {
+            constexpr int J = I - kNA - kNW;
+            const int seg = wave + J * NWAVES;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wside ? rws : ras,
+                                                     (lds_void *)((wside ? sws : sas) + seg * 64), 4,
+                                                     wside ? ows[J] : oas[J],
+                                                     wside ? kbs * 4 : (kbs >> a_shift) * 4, 0, 0);
         }
     }
 
@@ -150,30 +200,34 @@ struct BufStage {
     // 256 bytes per scale-segment instruction; segment `seg` of an operand is
     // issued by wave seg % NWAVES.
     __device__ __forceinline__ void issue(Stage<BM, BN> &st, uint32_t kb, int wave) const {
+        issue_parts(st.a, st.w, &st.as[0][0], &st.ws[0][0], kb, wave);
+    }
+    __device__ __forceinline__ void issue_parts(int8_t *sta, int8_t *stw, float *stas, float *stws, uint32_t kb,
+                                                int wave) const {
 #pragma unroll
         for (int i = 0; i < kNA; ++i) {
             const int seg = wave + i * NWAVES;
             if (kSegA % NWAVES != 0 && seg >= kSegA) break;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st.a + seg * 1024), 16, oa[i], kb * 32, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(sta + seg * 1024), 16, oa[i], kb * 32, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < kNW; ++i) {
             const int seg = wave + i * NWAVES;
             if (kSegW % NWAVES != 0 && seg >= kSegW) break;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(st.w + seg * 1024), 16, ow[i], kb * 32, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(stw + seg * 1024), 16, ow[i], kb * 32, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < kNAs; ++i) {
             const int seg = wave + i * NWAVES;
             if (kSegAs % NWAVES != 0 && seg >= kSegAs) break;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_void *)(&st.as[0][0] + seg * 64), 4, oas[i],
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_void *)(stas + seg * 64), 4, oas[i],
                                                      (kb >> a_shift) * 4, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < kNWs; ++i) {
             const int seg = wave + i * NWAVES;
             if (kSegWs % NWAVES != 0 && seg >= kSegWs) break;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rws, (lds_void *)(&st.ws[0][0] + seg * 64), 4, ows[i], kb * 4,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rws, (lds_void *)(stws + seg * 64), 4, ows[i], kb * 4,
                                                      0, 0);
         }
     }
@@ -259,12 +313,22 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
     using G = Geo<BM, BN, WM, WN>;
     constexpr int TM = G::kTM, TN = G::kTN;
     using St = Stage<BM, BN>;
-    __shared__ __attribute__((aligned(1024))) St rings[KG][RING];
+    // 128 x 128 with a ring of 2 (kSc8): operands in two OpStage buffers,
+    // scales in two Sc8Stage buffers, the next stage's copies spread over the
+    // first pair's units
+    constexpr bool kSc8 = RING == 2 && KG == 1 && !SPLIT && BM == 128 && BN == 128;
+    using Op = OpStage<BM, BN>;
+    using Sc = Sc8Stage<BM, BN>;
+    constexpr size_t kLds = kSc8 ? 2 * sizeof(Op) + 2 * sizeof(Sc) : sizeof(St) * KG * RING;
+    __shared__ __attribute__((aligned(1024))) char lds[kLds];
+    St(*rings)[RING] = reinterpret_cast<St(*)[RING]>(lds);
+    Op *ops = reinterpret_cast<Op *>(lds);
+    Sc *scs = reinterpret_cast<Sc *>(lds + 2 * sizeof(Op));
     static_assert(RING >= 2, "a ring of at least two buffers");
     static_assert(RING == 2 || even_copies<G, BM, BN>(), "deeper rings count uniform copies per wave");
     constexpr int kCopies = stage_copies<G, BM, BN>();
     static_assert(kCopies * (RING - 2) < 64, "the copies in flight fit the vmcnt range");
-    static_assert(KG == 1 || sizeof(rings) >= sizeof(float) * KG * BM * BN, "the reduction reuses the rings");
+    static_assert(KG == 1 || kLds >= sizeof(float) * KG * BM * BN, "the reduction reuses the rings");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -317,13 +381,26 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
 
     const v16i zero16 = {};
     const v32f zero32 = {};
+    BufStage<BM, BN, G::kWaves, kSc8> bufst;
+    bufst.init(a, w, a_s, w_s, M, N, K, nb, a_ld, a_shift, m0, n0, wave, lane);
+    // the next stage's copies (kSc8): operand slot, scale half, blocks
+    int8_t *nx_a = nullptr, *nx_w = nullptr;
+    float *nx_as = nullptr, *nx_ws = nullptr;
+    uint32_t nx_kb = 0, nx_kbs = 0;
+    bool nx_wside = false;
+    constexpr int kScRow = kSc8 ? kSc8Blocks : kGemmStageBlocks;
+    auto sidx = [&](uint32_t row, uint32_t blk) {
+        return row * kScRow + (blk ^ (kSc8 ? scale_swz8(row) : scale_swz(row)));
+    };
 
     // A block pair (blocks jp, jp + 1 of the stage) = 2 * TM * TN units (tile
     // t = sm * TN + sn, block j).  The matrix-core result of unit u + 1 (and the
     // scale products of its tile) is requested before unit u is rescaled, so
     // each rescale reads a result that finished while the previous unit's 32
     // VALU instructions ran.
-    auto pair = [&](const St &cur, uint32_t kb, int jp) {
+    // operands ca / cw, scale rows cas / cws whose block boff is the stage's first
+    auto pair = [&](const int8_t *ca, const int8_t *cw, const float *cas, const float *cws, uint32_t boff,
+                    uint32_t kb, int jp) __attribute__((always_inline)) {
         v4i af[TM][2], bf[TN][2];
         float asv[TM], wsv[TN];
         // lanes 0-31 carry block jp, lanes 32-63 block jp + 1 (zero if past
@@ -333,18 +410,18 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
         for (int t = 0; t < TM; ++t) {
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                af[t][j] = *reinterpret_cast<const v4i *>(cur.a + off_a[jp + j] + t * 32 * kGemmStageBytes);
+                af[t][j] = *reinterpret_cast<const v4i *>(ca + off_a[jp + j] + t * 32 * kGemmStageBytes);
             const uint32_t ra = wm * WM + t * 32 + (lane & 31);
-            const float av = cur.as[ra][(jp + half) ^ scale_swz(ra)];
+            const float av = cas[sidx(ra, boff + jp + half)];
             asv[t] = blk_live ? av : 0.0f;
         }
 #pragma unroll
         for (int t = 0; t < TN; ++t) {
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                bf[t][j] = *reinterpret_cast<const v4i *>(cur.w + off_w[jp + j] + t * 32 * kGemmStageBytes);
+                bf[t][j] = *reinterpret_cast<const v4i *>(cw + off_w[jp + j] + t * 32 * kGemmStageBytes);
             const uint32_t rw = wn * WN + t * 32 + (lane & 31);
-            wsv[t] = cur.ws[rw][(jp + half) ^ scale_swz(rw)];
+            wsv[t] = cws[sidx(rw, boff + jp + half)];
         }
         constexpr int kUnits = 2 * TM * TN;
         v32f sc[2];
@@ -366,15 +443,34 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
                     __builtin_amdgcn_mfma_i32_32x32x32_i8(af[t1 / TN][j1], bf[t1 % TN][j1], zero16, 0, 0, 0);
                 __builtin_amdgcn_s_setprio(0);
             }
+            if constexpr (kSc8) {
+                // the first pair's units issue the next stage's 12 copies:
+                // units 0-3 two each, 4-7 one each
+                if (jp == 0) {
+#define BSR_ONE(I) bufst.template issue_one<I>(nx_a, nx_w, nx_as, nx_ws, nx_kb, nx_kbs, nx_wside, wave)
+                    switch (u) {
+                    case 0: BSR_ONE(0); BSR_ONE(1); break;
+                    case 1: BSR_ONE(2); BSR_ONE(3); break;
+                    case 2: BSR_ONE(4); BSR_ONE(5); break;
+                    case 3: BSR_ONE(6); BSR_ONE(7); break;
+                    case 4: BSR_ONE(8); break;
+                    case 5: BSR_ONE(9); break;
+                    case 6: BSR_ONE(10); break;
+                    default: BSR_ONE(11); break;
+                    }
+#undef BSR_ONE
+                }
+            }
             float *ac = acc[t / TN][t % TN];
 #pragma unroll
             for (int r = 0; r < 16; ++r) ac[r] = fmaf((float)p[u & 1][r], sc[t & 1][16 * j + r], ac[r]);
         }
     };
-    auto compute = [&](const St &cur, uint32_t kb) {
+    auto compute = [&](const int8_t *ca, const int8_t *cw, const float *cas, const float *cws, uint32_t boff,
+                       uint32_t kb) {
 #pragma unroll
         for (int jp = 0; jp < kGemmStageBlocks; jp += 2) {
-            pair(cur, kb, jp);
+            pair(ca, cw, cas, cws, boff, kb, jp);
             // read the next pair's operands only after this pair: bounds live registers
             asm volatile("" ::: "memory");
         }
@@ -383,8 +479,6 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
 #pragma unroll
             for (int j = 0; j < TN; ++j) BSR_PIN16(acc[i][j]);
     };
-    BufStage<BM, BN, G::kWaves> bufst;
-    bufst.init(a, w, a_s, w_s, M, N, K, nb, a_ld, a_shift, m0, n0, wave, lane);
     auto issue = [&](St &buf, uint32_t stage) { bufst.issue(buf, (s_first + stage) * kGemmStageBlocks, wave); };
     // Stage s lives in buffer s % RING.  At the top of stage s each wave waits
     // for its own copies of stage s (those of the up to RING - 2 later stages
@@ -394,12 +488,42 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
     auto step = [&](int u, uint32_t s) {
         wait_later_stages<kCopies, RING - 2>(s < nstages ? min(nstages - 1 - s, (uint32_t)RING - 2) : 0);
         stage_barrier();
-        if (s + RING - 1 < nstages) issue(ring[(u + RING - 1) % RING], s + RING - 1);
-        if (!kRange || s < nstages) compute(ring[u], (s_first + s) * kGemmStageBlocks);
+        if constexpr (kSc8) {
+            // Stage s reads operand slot u and scale stage s / 2 (blocks from
+            // (s % 2) * 4).  Its units bring stage s + 1's operands into the
+            // other slot and half of a later scale stage: for odd s + 1 the A
+            // rows of scale stage (s + 2) / 2, for even s + 1 the W rows of
+            // scale stage (s + 1) / 2 -- each into the buffer the stage before
+            // last finished with.  Past the last stage the copies re-read
+            // in-range blocks into buffers nobody reads any more.
+            const uint32_t last = nstages - 1;
+            const uint32_t nx = s + 1;
+            nx_a = ops[(u + 1) % 2].a;
+            nx_w = ops[(u + 1) % 2].w;
+            nx_kb = min(nx, last) * kGemmStageBlocks;
+            nx_wside = nx % 2 == 0;
+            const uint32_t sst = nx_wside ? nx / 2 : (nx + 1) / 2;
+            nx_as = &scs[sst % 2].as[0][0];
+            nx_ws = &scs[sst % 2].ws[0][0];
+            nx_kbs = min(2 * sst, last) * kGemmStageBlocks;
+            const Sc &sc = scs[(s / 2) % 2];
+            compute(ops[u].a, ops[u].w, &sc.as[0][0], &sc.ws[0][0], (s % 2) * kGemmStageBlocks,
+                    s * kGemmStageBlocks);
+        } else {
+            if (s + RING - 1 < nstages) issue(ring[(u + RING - 1) % RING], s + RING - 1);
+            if (!kRange || s < nstages)
+                compute(ring[u].a, ring[u].w, &ring[u].as[0][0], &ring[u].ws[0][0], 0,
+                        (s_first + s) * kGemmStageBlocks);
+        }
     };
+    if constexpr (kSc8) {
+        // stage 0's operands and both halves of scale stage 0
+        bufst.issue_parts(ops[0].a, ops[0].w, &scs[0].as[0][0], &scs[0].ws[0][0], 0, wave);
+    } else {
 #pragma unroll
-    for (int r = 0; r < RING - 1; ++r)
-        if ((!kRange && r == 0) || (uint32_t)r < nstages) issue(ring[r], r);  // (no split: K has a stage)
+        for (int r = 0; r < RING - 1; ++r)
+            if ((!kRange && r == 0) || (uint32_t)r < nstages) issue(ring[r], r);  // (no split: K has a stage)
+    }
     for (uint32_t s = 0; s < spg; s += RING) {
 #pragma unroll
         for (int u = 0; u < RING; ++u) {
@@ -407,12 +531,13 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
             step(u, s + u);
         }
     }
+    if constexpr (kSc8) wait_copies<0>();  // the copies issued by the last stage land before the workgroup ends
 
     if constexpr (KG > 1) {
         // Groups' tiles through LDS (the rings are free once every wave has
         // passed this barrier), summed in group order by group 0.
         __syncthreads();
-        float *red = reinterpret_cast<float *>(&rings[0][0]);
+        float *red = reinterpret_cast<float *>(lds);
         constexpr int kTile = TM * TN * 16;  // floats per lane
         const uint32_t slot = (uint32_t)(wave * 64 + lane) * kTile;
         constexpr uint32_t kGroupFloats = G::kWaves * 64 * kTile;

@@ -423,3 +423,51 @@ def test_gemm_split_k_errors_and_no_split():
     got = canary_out(m2, n2)
     bsr.int8_gemm_blockscaled_ws(da, dw, das, dws, got, None)
     assert np.array_equal(host(got), host(ref))
+
+
+def _padded(arr, fill, pad_bytes=512):
+    """A device copy of `arr` followed, in the same allocation, by pad_bytes of
+    `fill`: reads past the tensor's end stay inside memory the test owns."""
+    flat = torch.from_numpy(np.ascontiguousarray(arr).ravel())
+    extra = pad_bytes // flat.element_size()
+    buf = torch.full((flat.numel() + extra,), fill, dtype=flat.dtype, device=DEV)
+    buf[:flat.numel()] = flat.to(DEV)
+    return buf[:flat.numel()].view(arr.shape)
+
+
+# Inputs followed by poison (NaN scales, 0x7F codes) with K tails in a later
+# stage: the K tail of a tile's last row reads past the row's end, which the
+# buffer range check turns into zeros; anything else would bring NaN into the
+# FP32 sums (a zeroed activation-scale product times a NaN weight scale).  The
+# big-tile shape stages scales 8 blocks at a time, so 13 blocks leave 3 past
+# the end of its second scale stage; the small-grid and GEMV shapes run too.
+@pytest.mark.parametrize("m,n,k,path", [(1100, 7400, 416, bsr.PATH_GEMM), (300, 260, 160, bsr.PATH_GEMM),
+                                        (40, 70, 160, bsr.PATH_AUTO), (8, 70, 416, bsr.PATH_AUTO),
+                                        (8, 70, 160, bsr.PATH_INVARIANT), (20, 300, 224, bsr.PATH_INVARIANT)])
+def test_tail_reads_ignore_bytes_past_buffers(m, n, k, path):
+    say(f"poisoned tails m={m} n={n} k={k} path={path}")
+    a, w, a_s, w_s = _rand_operands(m + n + k, m, n, k)
+    out = canary_out(m, n)
+    bsr.int8_gemm_blockscaled_ex(_padded(a, 0x7F), _padded(w, 0x7F), _padded(a_s, float("nan")),
+                                 _padded(w_s, float("nan")), out, path=path)
+    y, t = oracle.gemm_ref(a, w, a_s, w_s)
+    _check(f"poisoned tails {m}x{n}x{k}", host(out), y, t, k)
+
+
+def test_tail_reads_ignore_bytes_past_buffers_agroup():
+    """The same with activation scales per 128 elements and per row on the big
+    tiles: K = 1152 is 36 blocks, 9 stages, so the last 8-block scale stage
+    holds 4 blocks past the end (one 128-element group past each row)."""
+    m, n, k = 1100, 7400, 1152
+    a, w, _, w_s = _rand_operands(77, m, n, k)
+    rng = np.random.default_rng(78)
+    rows = np.array([0, 127, 128, 1023, 1024, 1099])
+    for group in (128, 0):
+        ng = 1 if group == 0 else k // group
+        a_s = (rng.uniform(0.5, 2.0, size=(m, ng)) * 2.0 ** -8).astype(np.float32)
+        say(f"poisoned tails, activation scale group {group}")
+        out = canary_out(m, n)
+        bsr.int8_gemm_blockscaled_agroup(_padded(a, 0x7F), _padded(w, 0x7F), _padded(a_s, float("nan")), group,
+                                         _padded(w_s, float("nan")), out, path=bsr.PATH_GEMM)
+        y, t = oracle.gemm_ref_agroup(a, w, a_s, w_s, group if group else k, rows=rows)
+        _check(f"poisoned tails agroup {group}", host(out)[rows], y, t, k)
