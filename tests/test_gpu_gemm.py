@@ -440,8 +440,10 @@ def _padded(arr, fill, pad_bytes=512):
 # buffer range check turns into zeros; anything else would bring NaN into the
 # FP32 sums (a zeroed activation-scale product times a NaN weight scale).  The
 # big-tile shape stages scales 8 blocks at a time, so 13 blocks leave 3 past
-# the end of its second scale stage; the small-grid and GEMV shapes run too.
-@pytest.mark.parametrize("m,n,k,path", [(1100, 7400, 416, bsr.PATH_GEMM), (300, 260, 160, bsr.PATH_GEMM),
+# the end of its second scale stage (1 block: one stage; 7 blocks: two stages
+# in one scale stage); the small-grid and GEMV shapes run too.
+@pytest.mark.parametrize("m,n,k,path", [(1100, 7400, 416, bsr.PATH_GEMM), (1100, 7400, 32, bsr.PATH_GEMM),
+                                        (1100, 7400, 224, bsr.PATH_GEMM), (300, 260, 160, bsr.PATH_GEMM),
                                         (40, 70, 160, bsr.PATH_AUTO), (8, 70, 416, bsr.PATH_AUTO),
                                         (8, 70, 160, bsr.PATH_INVARIANT), (20, 300, 224, bsr.PATH_INVARIANT)])
 def test_tail_reads_ignore_bytes_past_buffers(m, n, k, path):
