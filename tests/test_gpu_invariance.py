@@ -149,10 +149,13 @@ def test_invariant_path_errors():
     assert torch.all(out == 0)
 
 
-def test_rows_equal_across_gemm_tile_shapes():
+@pytest.mark.parametrize("k", [512, 544])
+def test_rows_equal_across_gemm_tile_shapes(k):
     """A 2048-row GEMM at N = 4096 runs 128x128 tiles; 100 of its rows alone run
-    64x64 tiles, and 16 of them the chain GEMV: the same bits every time."""
-    m, n, k = 2048, 4096, 512
+    64x64 tiles, and 16 of them the chain GEMV: the same bits every time.  The
+    128x128 tiles stage scales 8 blocks at a time: K = 544 (17 blocks, 5
+    stages) ends in a scale stage with one live block."""
+    m, n = 2048, 4096
     a, packed, e4m3 = _operands(11, m, n, k)
     w_i8, w_s = gpu_requant_w(packed, e4m3, inputs.SCALE2_1_448)
     a_i8, a_s = gpu_requant_a(a)
