@@ -86,13 +86,19 @@ constexpr uint32_t kLdsBytes = 160u * 1024u;  // LDS of one CU (gfx950)
 constexpr uint32_t kSplitTile = 64;
 constexpr uint32_t kSplitMaxWorkgroups = 2 * kGemmCus;  // two workgroups per CU
 constexpr uint32_t kSplitMaxSlices = 16;
-constexpr uint32_t kSplitMinStages = 4;                 // K stages per slice, at least
+// K stages per slice, at least: slices of 4 stages spent more on each
+// slice's pipeline start than they gained in workgroups (n = 2048,
+// k = 8192, m = 40 / 48 / 64: 16.3 / 17.0 / 18.1 us with 16 slices of 4
+// stages, 13.1 / 13.3 / 13.9 with 8 of 8, against 15.3 / 15.8 / 19.9 without
+// workspace)
+constexpr uint32_t kSplitMinStages = 8;
 // Where the split measured faster than the paths without workspace: more
 // rows than the streamed GEMV's two 16-row tiles, and K long enough (64
 // stages, K >= 8192) to hide each slice's pipeline start and the second
-// launch (n = 4096, k = 14336: m = 48 / 64 / 128 / 192 in 25.5 / 27.0 / 39.3 /
-// 60.2 us against 26.6 / 33.8 / 54.1 / 67.3; n = 14336, k = 4096, m = 17-64:
-// 1.4-1.8 us slower; m = 17-32 at n = 4096: 1.7-3.3 us slower).
+// launch (n = 4096, k = 14336: m = 40 / 48 / 64 / 128 in 22.4 / 23.4 / 24.6 /
+// 34.5 us against 25.0 / 26.5 / 33.7 / 54.4; m = 17-32 at n = 4096: level to
+// 2.4 us slower; at k = 4096, n = 4096, m <= 64: 1.7-2.3 us slower, n = 14336,
+// m = 40-64: 1-2 % faster).
 constexpr uint32_t kSplitMinRows = 33;
 constexpr uint32_t kSplitMinKStages = 64;
 constexpr uint64_t kSplitMaxBytes = (uint64_t)kSplitMaxWorkgroups * kSplitTile * kSplitTile * 4;

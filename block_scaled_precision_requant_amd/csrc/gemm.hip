@@ -172,27 +172,64 @@ struct BufStage {
         }
     }
 
-    // SC8, one copy I (compile-time) of a stage's 12: the 8 operand segments
-    // of the stage from block kb into (sa, sw), then 4 scale copies -- the A
-    // scale rows of the 8 blocks from kbs into sas when !wside, else the W
-    // scale rows into sws (every count divides evenly among the 4 waves).
+    // SC8, one copy I (compile-time) of a stage's kAll: the operand segments
+    // of the stage from block kb into (sa, sw), then the wave's copies of half
+    // a scale stage -- the A scale rows of the 8 blocks from kbs into sas when
+    // !wside, else the W scale rows into sws (every count divides evenly among
+    // the waves, and the two halves are equal).
+    static constexpr int kAll = kNA + kNW + kNAs;
     template <int I>
     __device__ __forceinline__ void issue_one(int8_t *sa, int8_t *sw, float *sas, float *sws, uint32_t kb,
                                               uint32_t kbs, bool wside, int wave) const {
-        static_assert(SC8 && NWAVES == 4 && kNA == 4 && kNW == 4 && kNAs == 4 && kNWs == 4, "the 128 x 128 shape");
+        static_assert(SC8 && kSegA % NWAVES == 0 && kSegW % NWAVES == 0 && kSegAs % NWAVES == 0 &&
+                          kSegWs % NWAVES == 0 && kNAs == kNWs,
+                      "uniform copies, equal scale halves");
         if constexpr (I < kNA) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(sa + (wave + I * NWAVES) * 1024), 16, oa[I],
                                                      kb * 32, 0, 0);
         } else if constexpr (I < kNA + kNW) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(sw + (wave + (I - kNA) * NWAVES) * 1024), 16,
                                                      ow[I - kNA], kb * 32, 0, 0);
-        } else {
+        } else if constexpr (I < kAll) {
             constexpr int J = I - kNA - kNW;
             const int seg = wave + J * NWAVES;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(wside ? rws : ras,
                                                      (lds_void *)((wside ? sws : sas) + seg * 64), 4,
                                                      wside ? ows[J] : oas[J],
                                                      wside ? kbs * 4 : (kbs >> a_shift) * 4, 0, 0);
+        }
+    }
+
+    // SC8, all of a stage's copies: its operands and the wave's copies of one
+    // scale half (as issue_one over [0, kAll))
+    __device__ __forceinline__ void issue_stage(int8_t *sa, int8_t *sw, float *sas, float *sws, uint32_t kb,
+                                               uint32_t kbs, bool wside, int wave) const {
+        if (sa != nullptr) {
+#pragma unroll
+            for (int i = 0; i < kNA; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(sa + (wave + i * NWAVES) * 1024), 16, oa[i],
+                                                         kb * 32, 0, 0);
+#pragma unroll
+            for (int i = 0; i < kNW; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(sw + (wave + i * NWAVES) * 1024), 16, ow[i],
+                                                         kb * 32, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < kNAs; ++j) {
+            const int seg = wave + j * NWAVES;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wside ? rws : ras, (lds_void *)((wside ? sws : sas) + seg * 64),
+                                                     4, wside ? ows[j] : oas[j],
+                                                     wside ? kbs * 4 : (kbs >> a_shift) * 4, 0, 0);
+        }
+    }
+
+    // copies [LO, HI) of a stage
+    template <int LO, int HI>
+    __device__ __forceinline__ void issue_range(int8_t *sa, int8_t *sw, float *sas, float *sws, uint32_t kb,
+                                                uint32_t kbs, bool wside, int wave) const {
+        if constexpr (LO < HI) {
+            issue_one<LO>(sa, sw, sas, sws, kb, kbs, wside, wave);
+            issue_range<LO + 1, HI>(sa, sw, sas, sws, kb, kbs, wside, wave);
         }
     }
 
@@ -289,6 +326,11 @@ __device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "
                  "+v"(x[6]), "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]),    \
                  "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15]))
 
+// The first of C copies that unit g of U issues: two each for the first
+// C - U units, one each after them (C <= 2 U).
+template <int C, int U>
+constexpr int spread_first(int g) { return g + (g < C - U ? g : C - U); }
+
 }  // namespace
 
 namespace gemm_kernels {
@@ -313,17 +355,24 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
     using G = Geo<BM, BN, WM, WN>;
     constexpr int TM = G::kTM, TN = G::kTN;
     using St = Stage<BM, BN>;
-    // 128 x 128 with a ring of 2 (kSc8): operands in two OpStage buffers,
-    // scales in two Sc8Stage buffers, the next stage's copies spread over the
-    // first pair's units
-    constexpr bool kSc8 = RING == 2 && KG == 1 && !SPLIT && BM == 128 && BN == 128;
+    // kSc8 -- the 128 x 128 shape with a ring of 2 and the K-split 64 x 64
+    // shape with a ring of 4: operands in RING OpStage buffers, scales in
+    // Sc8Stage buffers of 8 blocks (2 for a ring of 2; 3 for a ring of 4,
+    // whose copies run three stages ahead), and each stage's copies spread
+    // over the units that compute the stage before them.
+    constexpr bool kSc8 = (RING == 2 && KG == 1 && !SPLIT && BM == 128 && BN == 128) ||
+                          (RING == 4 && SPLIT && BM == 64 && BN == 64);
+    constexpr int kScBufs = RING == 2 ? 2 : 3;
+    // units that carry the copies: a ring of 2 leaves the copies one stage to
+    // land, so only the first pair's units carry them; a ring of 4, all units
+    constexpr int kSpreadUnits = RING == 2 ? 2 * TM * TN : 4 * TM * TN;
     using Op = OpStage<BM, BN>;
     using Sc = Sc8Stage<BM, BN>;
-    constexpr size_t kLds = kSc8 ? 2 * sizeof(Op) + 2 * sizeof(Sc) : sizeof(St) * KG * RING;
+    constexpr size_t kLds = kSc8 ? RING * sizeof(Op) + kScBufs * sizeof(Sc) : sizeof(St) * KG * RING;
     __shared__ __attribute__((aligned(1024))) char lds[kLds];
     St(*rings)[RING] = reinterpret_cast<St(*)[RING]>(lds);
     Op *ops = reinterpret_cast<Op *>(lds);
-    Sc *scs = reinterpret_cast<Sc *>(lds + 2 * sizeof(Op));
+    Sc *scs = reinterpret_cast<Sc *>(lds + RING * sizeof(Op));
     static_assert(RING >= 2, "a ring of at least two buffers");
     static_assert(RING == 2 || even_copies<G, BM, BN>(), "deeper rings count uniform copies per wave");
     constexpr int kCopies = stage_copies<G, BM, BN>();
@@ -444,22 +493,31 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
                 __builtin_amdgcn_s_setprio(0);
             }
             if constexpr (kSc8) {
-                // the first pair's units issue the next stage's 12 copies:
-                // units 0-3 two each, 4-7 one each
-                if (jp == 0) {
-#define BSR_ONE(I) bufst.template issue_one<I>(nx_a, nx_w, nx_as, nx_ws, nx_kb, nx_kbs, nx_wside, wave)
-                    switch (u) {
-                    case 0: BSR_ONE(0); BSR_ONE(1); break;
-                    case 1: BSR_ONE(2); BSR_ONE(3); break;
-                    case 2: BSR_ONE(4); BSR_ONE(5); break;
-                    case 3: BSR_ONE(6); BSR_ONE(7); break;
-                    case 4: BSR_ONE(8); break;
-                    case 5: BSR_ONE(9); break;
-                    case 6: BSR_ONE(10); break;
-                    default: BSR_ONE(11); break;
-                    }
-#undef BSR_ONE
+                // unit g of the stage (over its pairs) issues copies
+                // [first(g), first(g + 1)) of the next stage's kAll: two each
+                // for the first kAll - kSpreadUnits units, then one each
+                using BS = decltype(bufst);
+                static_assert(BS::kAll >= kSpreadUnits && BS::kAll <= 2 * kSpreadUnits, "one or two per unit");
+                const int g = (jp / 2) * kUnits + u;
+#define BSR_UNIT(G)                                                                                   \
+    case G:                                                                                           \
+        if constexpr (G < kSpreadUnits)                                                               \
+            bufst.template issue_range<spread_first<BS::kAll, kSpreadUnits>(G),                        \
+                                       spread_first<BS::kAll, kSpreadUnits>(G + 1)>(                   \
+                nx_a, nx_w, nx_as, nx_ws, nx_kb, nx_kbs, nx_wside, wave);                            \
+        break;
+                switch (g) {
+                    BSR_UNIT(0)
+                    BSR_UNIT(1)
+                    BSR_UNIT(2)
+                    BSR_UNIT(3)
+                    BSR_UNIT(4)
+                    BSR_UNIT(5)
+                    BSR_UNIT(6)
+                    BSR_UNIT(7)
+                default: break;
                 }
+#undef BSR_UNIT
             }
             float *ac = acc[t / TN][t % TN];
 #pragma unroll
@@ -480,6 +538,24 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
             for (int j = 0; j < TN; ++j) BSR_PIN16(acc[i][j]);
     };
     auto issue = [&](St &buf, uint32_t stage) { bufst.issue(buf, (s_first + stage) * kGemmStageBlocks, wave); };
+    // kSc8: the copies of stage t are its operands (into slot t % RING) and
+    // half of a scale stage: for odd t the A rows of scale stage (t + 1) / 2,
+    // for even t the W rows of scale stage t / 2, so both halves of scale
+    // stage j have landed by the top of stage 2j, and each goes into the
+    // buffer scale stage j - kScBufs left, which the stages before the
+    // current one finished with.  Past the group's last stage the copies
+    // re-read in-range blocks into buffers nobody reads any more.
+    auto set_next = [&](uint32_t t) {
+        const uint32_t last = nstages - 1;
+        nx_a = ops[t % RING].a;
+        nx_w = ops[t % RING].w;
+        nx_kb = (s_first + min(t, last)) * kGemmStageBlocks;
+        nx_wside = t % 2 == 0;
+        const uint32_t sst = nx_wside ? t / 2 : (t + 1) / 2;
+        nx_as = &scs[sst % kScBufs].as[0][0];
+        nx_ws = &scs[sst % kScBufs].ws[0][0];
+        nx_kbs = (s_first + min(2 * sst, last)) * kGemmStageBlocks;
+    };
     // Stage s lives in buffer s % RING.  At the top of stage s each wave waits
     // for its own copies of stage s (those of the up to RING - 2 later stages
     // already issued may stay in flight), the barrier publishes every wave's
@@ -490,25 +566,13 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
         stage_barrier();
         if constexpr (kSc8) {
             // Stage s reads operand slot u and scale stage s / 2 (blocks from
-            // (s % 2) * 4).  Its units bring stage s + 1's operands into the
-            // other slot and half of a later scale stage: for odd s + 1 the A
-            // rows of scale stage (s + 2) / 2, for even s + 1 the W rows of
-            // scale stage (s + 1) / 2 -- each into the buffer the stage before
-            // last finished with.  Past the last stage the copies re-read
-            // in-range blocks into buffers nobody reads any more.
-            const uint32_t last = nstages - 1;
-            const uint32_t nx = s + 1;
-            nx_a = ops[(u + 1) % 2].a;
-            nx_w = ops[(u + 1) % 2].w;
-            nx_kb = min(nx, last) * kGemmStageBlocks;
-            nx_wside = nx % 2 == 0;
-            const uint32_t sst = nx_wside ? nx / 2 : (nx + 1) / 2;
-            nx_as = &scs[sst % 2].as[0][0];
-            nx_ws = &scs[sst % 2].ws[0][0];
-            nx_kbs = min(2 * sst, last) * kGemmStageBlocks;
-            const Sc &sc = scs[(s / 2) % 2];
-            compute(ops[u].a, ops[u].w, &sc.as[0][0], &sc.ws[0][0], (s % 2) * kGemmStageBlocks,
-                    s * kGemmStageBlocks);
+            // (s % 2) * 4); its units bring the copies of stage s + RING - 1.
+            set_next(s + RING - 1);
+            if (!kRange || s < nstages) {
+                const Sc &sc = scs[(s / 2) % kScBufs];
+                compute(ops[u].a, ops[u].w, &sc.as[0][0], &sc.ws[0][0], (s % 2) * kGemmStageBlocks,
+                        (s_first + s) * kGemmStageBlocks);
+            }
         } else {
             if (s + RING - 1 < nstages) issue(ring[(u + RING - 1) % RING], s + RING - 1);
             if (!kRange || s < nstages)
@@ -517,8 +581,14 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
         }
     };
     if constexpr (kSc8) {
-        // stage 0's operands and both halves of scale stage 0
-        bufst.issue_parts(ops[0].a, ops[0].w, &scs[0].as[0][0], &scs[0].ws[0][0], 0, wave);
+        // the A half of scale stage 0 (stage 0's copies bring its W half), then
+        // the copies of stages 0 .. RING - 2
+        bufst.issue_stage(nullptr, nullptr, &scs[0].as[0][0], nullptr, 0, s_first * kGemmStageBlocks, false, wave);
+#pragma unroll
+        for (int t = 0; t < RING - 1; ++t) {
+            set_next(t);
+            bufst.issue_stage(nx_a, nx_w, nx_as, nx_ws, nx_kb, nx_kbs, nx_wside, wave);
+        }
     } else {
 #pragma unroll
         for (int r = 0; r < RING - 1; ++r)
