@@ -355,13 +355,13 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
     using G = Geo<BM, BN, WM, WN>;
     constexpr int TM = G::kTM, TN = G::kTN;
     using St = Stage<BM, BN>;
-    // kSc8 -- the 128 x 128 shape with a ring of 2 and the K-split 64 x 64
-    // shape with a ring of 4: operands in RING OpStage buffers, scales in
+    // kSc8 -- the 128 x 128 shape with a ring of 2 and the 64 x 64 shape with
+    // a ring of 4 (K split or not): operands in RING OpStage buffers, scales in
     // Sc8Stage buffers of 8 blocks (2 for a ring of 2; 3 for a ring of 4,
     // whose copies run three stages ahead), and each stage's copies spread
     // over the units that compute the stage before them.
     constexpr bool kSc8 = (RING == 2 && KG == 1 && !SPLIT && BM == 128 && BN == 128) ||
-                          (RING == 4 && SPLIT && BM == 64 && BN == 64);
+                          (RING == 4 && KG == 1 && BM == 64 && BN == 64);
     constexpr int kScBufs = RING == 2 ? 2 : 3;
     // units that carry the copies: a ring of 2 leaves the copies one stage to
     // land, so only the first pair's units carry them; a ring of 4, all units
@@ -686,7 +686,7 @@ BSR_GEMM_INST(128, 128, 64, 64, 2, 1, 2, false)
 BSR_GEMM_INST(32, 32, 32, 32, 1, 8, 2, false)
 BSR_GEMM_INST(32, 32, 32, 32, 2, 4, 2, false)
 BSR_GEMM_INST(64, 64, 32, 32, 1, 2, 3, false)
-BSR_GEMM_INST(64, 64, 32, 32, 2, 1, 2, false)
+BSR_GEMM_INST(64, 64, 32, 32, 2, 1, 4, false)
 BSR_GEMM_INST(64, 64, 32, 32, 2, 1, 4, true)
 #undef BSR_GEMM_INST
 
@@ -721,8 +721,10 @@ hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_sc
     // 2048x4096x4096 and 4096x28672x4096).  Smaller grids -- every m <= 128,
     // and e.g. m = 512 at n = 4096 -- take 64x64 tiles of four 32x32 waves:
     // four times the workgroups, 1.1-2.5x faster from m = 17 to 1024 on the
-    // decode and attention widths.  Per output the blocks are accumulated in
-    // the same order in both, so the bits do not depend on the shape chosen.
+    // decode and attention widths; their 4-deep ring (three stages in flight)
+    // and 8-block scale stages fit 76 KB of LDS, two workgroups per CU.  Per
+    // output the blocks are accumulated in the same order in both, so the bits
+    // do not depend on the shape chosen.
     const uint64_t big_tiles = div_up(m, kGemmBM) * div_up(n, kGemmBN);
     if (m > (uint32_t)kGemmBM && big_tiles >= 2 * (uint64_t)kGemmCus)
         return launch_tiles<kGemmBM, kGemmBN, 64, 64, 2>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, a_ld,
@@ -748,8 +750,8 @@ hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_sc
     if (split_k && small_tiles <= (uint64_t)kGemmCus && stages >= 2)
         return launch_tiles<kGemmSmallTile, kGemmSmallTile, 32, 32, 1, 2, 3>(a_i8, w_i8, a_scale, w_scale, out, m,
                                                                              n, k, a_ld, a_shift, s);
-    return launch_tiles<kGemmSmallTile, kGemmSmallTile, 32, 32, 2>(a_i8, w_i8, a_scale, w_scale, out, m, n, k,
-                                                                   a_ld, a_shift, s);
+    return launch_tiles<kGemmSmallTile, kGemmSmallTile, 32, 32, 2, 1, 4>(a_i8, w_i8, a_scale, w_scale, out, m, n,
+                                                                         k, a_ld, a_shift, s);
 }
 
 hipError_t launch_gemm_split(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale,
