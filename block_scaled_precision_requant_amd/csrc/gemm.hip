@@ -88,9 +88,10 @@ struct Stage {
     float ws[BN][kGemmStageBlocks];
 };
 
-// The 128 x 128 shape keeps its scales apart from the operand ring: one
-// scale stage covers two operand stages (8 blocks, 32 bytes of every scale
-// row), so a scale copy touches 8 rows' cache lines instead of 16.  Its 8
+// The 128 x 128 shape (ring of 2) and the 64 x 64 shapes with a ring of 4
+// keep their scales apart from the operand ring: one scale stage covers two
+// operand stages (8 blocks, 32 bytes of every scale row), so a scale copy
+// touches 8 rows' cache lines instead of 16.  Its 8
 // blocks of row r are permuted by scale_swz8(r): 32 consecutive rows read at
 // one block then hit 32 distinct banks (32- or 64-bank LDS).
 template <int BM, int BN>
