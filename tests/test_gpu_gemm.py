@@ -40,8 +40,10 @@ def _check(name, out_bits, y, t, k):
 # 5 stages; 4128: 33 stages with a partial last one), empty groups, and K too
 # short to split (96, 32) are all here; (20, 14336, 4096) and (100, 3000,
 # 2048) take the 4-group 32x32 tiles, (128, 4200, 1024) and (37, 1000, 160)
-# the 2-group 64x64 tiles, (64, 4096, 4096) the 8-group 32x32 tiles.
-@pytest.mark.parametrize("m,n,k", [(16, 256, 512), (200, 300, 544), (129, 257, 96), (9, 33, 32),
+# the 2-group 64x64 tiles, (64, 4096, 4096) the 8-group 32x32 tiles; (600, 2000,
+# 1056) and (129, 257, 96) the 64x64 tiles with a 4-deep ring (320 and 15
+# tiles; 9 stages, the last scale stage holding one live block; one stage).
+@pytest.mark.parametrize("m,n,k", [(16, 256, 512), (200, 300, 544), (129, 257, 96), (9, 33, 32), (600, 2000, 1056),
                                    (1000, 130, 1024), (256, 128, 4096), (37, 1000, 160),
                                    (48, 1000, 14336), (17, 512, 4128), (100, 200, 1056), (300, 700, 2080),
                                    (20, 14336, 4096), (100, 3000, 2048), (128, 4200, 1024), (64, 4096, 4096)])
