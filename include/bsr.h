@@ -110,6 +110,10 @@ BSR_API int requant_a_int8(const uint16_t *a_bf16, int8_t *a_i8, float *a_scale,
  * summation order is the kernel's own (not part of the contract); the result
  * is within 4e-3 relative or 1 BF16 ulp of the FP64 value, or within the
  * worst-case FP32 error of a K/32-term sum where that is larger.
+ * Scales must be finite: a NaN or Inf in a_scale or w_scale is outside the
+ * contract and may make other rows' outputs non-finite too (the kernels read
+ * a few scales past a row's last block and zero their products by
+ * multiplying by 0).
  * m <= 16 (one 16-row matrix-core tile) runs the weight-streaming GEMV; so
  * does m <= 48 when k is a multiple of 256 and n <= 4096 (16-column
  * workgroups at most one per CU); other shapes run the MFMA GEMM.
