@@ -19,10 +19,11 @@
 // ring of RING buffers; the next RING - 1 stages are in flight while the
 // current one is computed, with one barrier per stage.  A copy costs about
 // one cycle of the CU's load path per cache line it touches, whatever its
-// bytes, so the large 128 x 128 shape stages its scales 8 blocks (32 bytes
-// of a row) at a time, every other stage, and spreads the next stage's copies
-// over the units of its first block pair instead of issuing them all after
-// the barrier, where the eight waves of a CU queued behind each other.
+// bytes, so the 128 x 128 shape and the 64 x 64 shape with a ring of 4 stage
+// their scales 8 blocks (32 bytes of a row) at a time, every other stage, and
+// spread the next stage's copies over the units that compute the stage before
+// it instead of issuing them all after the barrier, where the eight waves of
+// a CU queued behind each other.
 #include "bsr_internal.h"
 
 namespace bsr {
@@ -110,8 +111,9 @@ __device__ __forceinline__ uint32_t scale_swz8(uint32_t r) { return (r >> 2) & 7
 // Operand staging: buffer loads straight into LDS.  A wave's copy fills LDS
 // in lane order (16 bytes per lane for operand rows, 4 for scales); the lane
 // whose LDS slot is (row, slot) fetches chunk slot ^ chunk_swz(row), and scale
-// copies map consecutive lanes to the (swizzled) blocks of a row, so one copy
-// touches 16 rows' worth of contiguous bytes.  Every lane's byte offset within
+// copies map consecutive lanes to the (swizzled) blocks of a row: an operand
+// copy covers 8 rows, a scale copy 16 rows of 4 blocks (8 rows of 8 blocks in
+// the 8-block scale stages).  Every lane's byte offset within
 // its workgroup's rows is fixed for the whole K loop -- only the scalar K
 // offset of a stage changes -- so a stage's copies cost no vector address
 // arithmetic.  Each operand's buffer starts at the workgroup's first row and
@@ -716,7 +718,7 @@ hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_sc
                        uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
                        uint32_t k, bool split_k, hipStream_t s) {
     // Grids of at least two 128x128 tiles per CU: two 4-wave 128x128
-    // workgroups per CU (LDS 2 x 72 KB, 2 x 4 waves of about 230 VGPRs); their
+    // workgroups per CU (LDS 2 x 80 KB, 2 x 4 waves of 216 VGPRs); their
     // barriers fall at different times, so one computes while the other waits
     // (measured faster than one 8-wave 256x128 workgroup per CU at
     // 2048x4096x4096 and 4096x28672x4096).  Smaller grids -- every m <= 128,
