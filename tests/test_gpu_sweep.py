@@ -1,4 +1,4 @@
-"""A seeded sweep of random shapes through every GEMM entry point, each output
+"""Seeded sweeps of random shapes.  First through every GEMM entry point, each output
 compared in full with the CPU oracle's FP64 reference (pass rule in
 oracle/compare.py; outputs start as a NaN canary, so an element no launch wrote
 fails).  The shapes fall in the row ranges the dispatch separates (the GEMV's
@@ -11,9 +11,10 @@ import pytest
 import torch
 
 import oracle
-from block_scaled_precision_requant_amd import bsr
-from gpu_util import DEV, canary_out, host, say, to_dev
-from oracle.compare import check_bf16
+from block_scaled_precision_requant_amd import bsr, inputs
+from gpu_util import (DEV, canary_out, f32_bits, gpu_quant_act, gpu_requant_a, gpu_requant_w, gpu_silu_requant,
+                      gpu_w4a16, host, say, to_dev)
+from oracle.compare import check_bf16, w4a16_terms
 
 pytestmark = pytest.mark.gpu
 
@@ -81,3 +82,91 @@ def test_sweep(i, entry, m, n, k):
     res = check_bf16(got, y, t, k)
     say(f"  {res}")
     assert res.ok, f"case {i} {entry} {m}x{n}x{k}: {res}"
+
+
+# The quantizers and the W4A16 GEMV over seeded random shapes: codes and scales
+# bit-exact against the oracle, W4A16 outputs by the pass rule.
+
+def _act(rng, m, k):
+    """BF16 activations with a magnitude per 32-block spanning 2^-30 .. 2^30,
+    some all-zero blocks and some blocks of BF16 subnormals."""
+    nb = k // 32
+    mag = 2.0 ** rng.integers(-30, 31, size=(m, nb, 1))
+    x = rng.standard_normal((m, nb, 32)) * mag
+    x[rng.random((m, nb)) < 0.03] = 0.0
+    tiny = rng.random((m, nb)) < 0.03
+    x[tiny] = rng.standard_normal((int(tiny.sum()), 32)) * 2.0 ** -130
+    return inputs.f32_to_bf16_bits(x.reshape(m, k).astype(np.float32))
+
+
+def _shape_cases(seed, count, m_hi, k_hi=600):
+    rng = np.random.default_rng(seed)
+    return [(i, int(rng.integers(1, m_hi + 1)), 32 * int(rng.integers(1, k_hi + 1))) for i in range(count)]
+
+
+@pytest.mark.parametrize("i,m,k", _shape_cases(11, 16, 400), ids=str)
+def test_sweep_requant_a(i, m, k):
+    say(f"sweep requant_a case {i}: m={m} k={k}")
+    a = _act(np.random.default_rng(2000 + i), m, k)
+    q, s = gpu_requant_a(a)
+    q_ref, s_ref = oracle.requant_a(a)
+    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(f32_bits(host(s)), f32_bits(s_ref))
+
+
+@pytest.mark.parametrize("i,n,k", _shape_cases(12, 16, 3000, k_hi=300), ids=str)
+def test_sweep_requant_w(i, n, k):
+    rng = np.random.default_rng(3000 + i)
+    scale2 = float(np.float32(rng.uniform(0.5, 2.0) * 2.0 ** int(rng.integers(-20, 8))))
+    say(f"sweep requant_w case {i}: n={n} k={k} scale2={scale2!r}")
+    packed = rng.integers(0, 256, size=(n, k // 2)).astype(np.uint8)
+    e4m3 = rng.integers(0, 0x7F, size=(n, k // 16)).astype(np.uint8)   # finite codes, both signs
+    e4m3 |= (rng.random(e4m3.shape) < 0.3).astype(np.uint8) << 7
+    q, s = gpu_requant_w(packed, e4m3, scale2)
+    q_ref, s_ref = oracle.requant_w(packed, e4m3, scale2)
+    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(f32_bits(host(s)), f32_bits(s_ref))
+
+
+@pytest.mark.parametrize("i,m,k", _shape_cases(13, 16, 300), ids=str)
+def test_sweep_silu_requant(i, m, k):
+    say(f"sweep silu requant case {i}: m={m} k={k}")
+    rng = np.random.default_rng(4000 + i)
+    gate = inputs.bf16_normal(rng, m, k, scale=float(2.0 ** rng.integers(-4, 5)))
+    up = inputs.bf16_normal(rng, m, k, scale=float(2.0 ** rng.integers(-4, 5)))
+    q, s = gpu_silu_requant(gate, up)
+    q_ref, s_ref = oracle.silu_mul_requant(gate, up)
+    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(f32_bits(host(s)), f32_bits(s_ref))
+
+
+@pytest.mark.parametrize("i,m,k", _shape_cases(14, 24, 300), ids=str)
+def test_sweep_quantize_act(i, m, k):
+    rng = np.random.default_rng(5000 + i)
+    group = (32, 128, 0)[i % 3]
+    if group == 128:
+        k = 128 * max(1, k // 128)
+    fmt, e4m3 = ((bsr.FMT_INT8, False), (bsr.FMT_E4M3, True))[(i // 3) % 2]
+    say(f"sweep quantize_act case {i}: m={m} k={k} group={group} e4m3={e4m3}")
+    a = _act(rng, m, k)
+    q, s = gpu_quant_act(a, group, fmt)
+    q_ref, s_ref = oracle.quant_act(a, k if group == 0 else group, e4m3=e4m3)
+    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(f32_bits(host(s)), f32_bits(s_ref))
+
+
+@pytest.mark.parametrize("i,m,k", _shape_cases(15, 16, 16, k_hi=300), ids=str)
+def test_sweep_w4a16(i, m, k):
+    rng = np.random.default_rng(6000 + i)
+    n = int(rng.integers(1, 3000))
+    if i % 2 == 0:
+        k = 256 * max(1, k // 256)        # the streamed kernel; odd cases mostly the register-decode one
+    say(f"sweep w4a16 case {i}: m={m} n={n} k={k}")
+    x = inputs.bf16_normal(rng, m, k)
+    wp, we = inputs.nvfp4_weight(rng, n, k, -4, 2)
+    codes = rng.integers(0, 0x7F, size=we.shape).astype(np.uint8)
+    we = np.where(rng.random(we.shape) < 0.5, codes, we).astype(np.uint8)
+    y, t = oracle.w4a16_ref(x, wp, we, inputs.SCALE2_1_448)
+    res = check_bf16(host(gpu_w4a16(x, wp, we, inputs.SCALE2_1_448)), y, t, k, terms=w4a16_terms(k))
+    say(f"  {res}")
+    assert res.ok, f"w4a16 case {i} {m}x{n}x{k}: {res}"
