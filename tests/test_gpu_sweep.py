@@ -170,3 +170,46 @@ def test_sweep_w4a16(i, m, k):
     res = check_bf16(host(gpu_w4a16(x, wp, we, inputs.SCALE2_1_448)), y, t, k, terms=w4a16_terms(k))
     say(f"  {res}")
     assert res.ok, f"w4a16 case {i} {m}x{n}x{k}: {res}"
+
+
+# Path invariance over seeded random shapes: under BSR_PATH_INVARIANT the rows
+# of an m <= 16 call (the chain GEMV) have the same bits as the same rows placed
+# at a random offset inside a larger call (the GEMM without its K split, 64 x 64
+# or 128 x 128 tiles as the grid decides), with grouped activation scales too.
+@pytest.mark.parametrize("i", range(24), ids=str)
+def test_sweep_invariance(i):
+    rng = np.random.default_rng(7000 + i)
+    m = int(rng.integers(1, 17))
+    big = int(rng.integers(17, 700))
+    n = int(rng.integers(1, 2600))
+    k = 32 * int(rng.integers(1, 300))
+    group = (32, 32, 128, 0)[i % 4]
+    if group == 128:
+        k = 128 * max(1, k // 128)
+    off = int(rng.integers(0, big - m + 1))
+    say(f"sweep invariance case {i}: m={m} inside {big} rows at {off}, n={n} k={k} group={group}")
+    ng = 1 if group == 0 else k // group
+    a = rng.integers(-127, 128, size=(big, k)).astype(np.int8)
+    w = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
+    a_s = (rng.uniform(0.5, 2.0, size=(big, ng)) * 2.0 ** rng.integers(-12, -2, size=(big, ng))).astype(np.float32)
+    w_s = (rng.uniform(0.5, 2.0, size=(n, k // 32)) * 2.0 ** rng.integers(-14, -4, size=(n, k // 32))
+           ).astype(np.float32)
+    da, dw, das, dws = to_dev(a), to_dev(w), to_dev(a_s), to_dev(w_s)
+    small = canary_out(m, n)
+    whole = canary_out(big, n)
+    sa, ssa = da[off:off + m].contiguous(), das[off:off + m].contiguous()
+    if group == 32:
+        bsr.int8_gemm_blockscaled_ex(sa, dw, ssa, dws, small, path=bsr.PATH_INVARIANT)
+        bsr.int8_gemm_blockscaled_ex(da, dw, das, dws, whole, path=bsr.PATH_INVARIANT)
+    else:
+        bsr.int8_gemm_blockscaled_agroup(sa, dw, ssa, group, dws, small, path=bsr.PATH_INVARIANT)
+        bsr.int8_gemm_blockscaled_agroup(da, dw, das, group, dws, whole, path=bsr.PATH_INVARIANT)
+    got_small, got_whole = host(small), host(whole)[off:off + m]
+    assert np.array_equal(got_small, got_whole), np.argwhere(got_small != got_whole)[:5]
+    sel = a[off:off + m], a_s[off:off + m]
+    if group == 32:
+        y, t = oracle.gemm_ref(sel[0], w, sel[1], w_s)
+    else:
+        y, t = oracle.gemm_ref_agroup(sel[0], w, sel[1], w_s, group if group else k)
+    res = check_bf16(got_small, y, t, k)
+    assert res.ok, res
