@@ -21,6 +21,15 @@ pytestmark = pytest.mark.gpu
 K_MAX_GEMM = (1 << 25) - 32
 
 
+@pytest.fixture(autouse=True)
+def _release_memory():
+    """These tests hold up to ~35 GB of device memory; hand it back to the
+    device after each, so later tests see the usual free memory."""
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
 def _gen(seed):
     g = torch.Generator(device=DEV)
     g.manual_seed(seed)
