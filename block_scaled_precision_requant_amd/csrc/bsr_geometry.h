@@ -31,11 +31,12 @@ constexpr int kSiluThreads = 512;    // lanes per workgroup of the SiLU table ke
 // made of 32 x 32 MFMA tiles.  The K loop stages kGemmStageBlocks 32-wide
 // blocks of A, W and their scales per LDS buffer, in a ring of 2 (or 3)
 // buffers.  Workgroups are ordered so that each XCD runs a compact
-// kGemmGroupM-tall group of output tiles.  Shapes: 128 x 128 with four
-// 64 x 64 waves, and 64 x 64 with four 32 x 32 waves for grids of the large
-// tile too small to give every CU two workgroups; both run two workgroups per
-// CU.  Grids with at most one or two tiles per CU split K inside the
-// workgroup over groups of waves (64 x 64 or 32 x 32 tiles).
+// kGemmGroupM-tall group of output tiles.  Shapes: 256 x 128 with eight
+// 64 x 64 waves, one workgroup per CU, and 128 x 128 with four 64 x 64 waves,
+// two per CU, for grids that give every CU two 128 x 128 tiles; 64 x 64 with
+// four 32 x 32 waves, two per CU, for smaller grids.  Grids with at most one
+// or two tiles per CU split K inside the workgroup over groups of waves
+// (64 x 64 or 32 x 32 tiles).
 constexpr int kGemmBM = 128;
 constexpr int kGemmBN = 128;
 constexpr int kGemmSmallTile = 64;
@@ -46,8 +47,20 @@ constexpr int kGemmGroupM = 8;
 constexpr int kXcds = 8;
 constexpr int kGemmCus = 256;                             // compute units of an MI355X
 // The GEMM stages operands with 32-bit buffer offsets from a tile's first row:
-// the rows of a tile (at most 128) must span less than 4 GiB, so k < 2^25.
+// the rows of a tile must span less than 4 GiB, so k < 2^25 for 128 rows.
 constexpr uint32_t kGemmMaxK = 1u << 25;
+
+// The tall tile, 256 x 128: per staged byte it computes a third more output
+// than the 128 x 128 tile (a copy's cost follows the cache lines it touches),
+// at the price of one workgroup per CU whose eight waves meet at every
+// barrier; measured 0.9-1.9 % faster at 2048x4096x4096, 4096x28672x4096 and
+// 8192x28672x8192, bit-identical.  Its XCD groups are 4 tile rows tall, so
+// an XCD's 32 concurrent tiles span 1024 A rows and 1024 W rows, and its 256
+// rows need k < 2^24.
+constexpr int kGemmTallBM = 256;
+constexpr int kGemmTallGroupM = 4;
+constexpr uint32_t kGemmTallMaxK = 1u << 24;
+
 
 // ---- GEMV (m <= 16) -------------------------------------------------------
 // A workgroup owns kGemvCols output columns and splits K over its waves; each
@@ -73,6 +86,16 @@ constexpr int kGemvBlocksPerIter = 4;   // K blocks per loop iteration of a wave
 constexpr int kW4PassSteps = 8;
 
 inline uint64_t div_up(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+// Grids that give every CU two 128 x 128 tiles (and m > 128) run the tall
+// tile when its 256-row tiling pads M no more than the 128-row one (m % 256
+// is 0 or above 128) and K allows it; else the 128 x 128 tile.
+inline bool gemm_big_tiles(uint32_t m, uint32_t n) {
+    return m > (uint32_t)kGemmBM && div_up(m, kGemmBM) * div_up(n, kGemmBN) >= 2 * (uint64_t)kGemmCus;
+}
+inline bool gemm_tall_tiles(uint32_t m, uint32_t n, uint32_t k) {
+    return gemm_big_tiles(m, n) && div_up(m, kGemmTallBM) * 2 == div_up(m, kGemmBM) && k < kGemmTallMaxK;
+}
 
 constexpr uint32_t kLdsBytes = 160u * 1024u;  // LDS of one CU (gfx950)
 

@@ -19,8 +19,9 @@
 // ring of RING buffers; the next RING - 1 stages are in flight while the
 // current one is computed, with one barrier per stage.  A copy costs about
 // one cycle of the CU's load path per cache line it touches, whatever its
-// bytes, so the 128 x 128 shape and the 64 x 64 shape with a ring of 4 stage
-// their scales 8 blocks (32 bytes of a row) at a time, every other stage, and
+// bytes, so the 256 x 128 and 128 x 128 shapes and the 64 x 64 shape with a
+// ring of 4 stage their scales 8 blocks (32 bytes of a row) at a time, every
+// other stage, and
 // spread the next stage's copies over the units that compute the stage before
 // it instead of issuing them all after the barrier, where the eight waves of
 // a CU queued behind each other.
@@ -53,17 +54,18 @@ struct Geo {
 
 // Workgroup -> output tile.  Workgroups are dispatched round-robin over the
 // XCDs; renumber them so each XCD gets a contiguous run, then walk the runs in
-// groups of kGemmGroupM tile rows so an XCD's concurrent tiles share A and W
-// rows in its L2.
+// groups of GROUP tile rows so an XCD's concurrent tiles share A and W rows in
+// its L2.
+template <uint32_t GROUP>
 __device__ __forceinline__ void tile_of(uint32_t wg, uint32_t tiles_m, uint32_t tiles_n,
                                         uint32_t &tm, uint32_t &tn) {
     const uint32_t total = tiles_m * tiles_n;
     const uint32_t q = total / kXcds, r = total % kXcds;
     const uint32_t x = wg % kXcds, j = wg / kXcds;
     const uint32_t v = x * q + min(x, r) + j;
-    const uint32_t per_group = kGemmGroupM * tiles_n;
-    const uint32_t first_m = (v / per_group) * kGemmGroupM;
-    const uint32_t gsize = min(tiles_m - first_m, (uint32_t)kGemmGroupM);
+    const uint32_t per_group = GROUP * tiles_n;
+    const uint32_t first_m = (v / per_group) * GROUP;
+    const uint32_t gsize = min(tiles_m - first_m, GROUP);
     const uint32_t in_group = v % per_group;
     tm = first_m + in_group % gsize;
     tn = in_group / gsize;
@@ -179,14 +181,16 @@ struct BufStage {
     // of the stage from block kb into (sa, sw), then the wave's copies of half
     // a scale stage -- the A scale rows of the 8 blocks from kbs into sas when
     // !wside, else the W scale rows into sws (every count divides evenly among
-    // the waves, and the two halves are equal).
-    static constexpr int kAll = kNA + kNW + kNAs;
+    // the waves; when the halves differ, as for 256 x 128 tiles, the smaller
+    // one skips its last copies).
+    static constexpr int kNSc = kNAs > kNWs ? kNAs : kNWs;  // copies of the larger scale half
+    static constexpr int kAll = kNA + kNW + kNSc;
     template <int I>
     __device__ __forceinline__ void issue_one(int8_t *sa, int8_t *sw, float *sas, float *sws, uint32_t kb,
                                               uint32_t kbs, bool wside, int wave) const {
         static_assert(SC8 && kSegA % NWAVES == 0 && kSegW % NWAVES == 0 && kSegAs % NWAVES == 0 &&
-                          kSegWs % NWAVES == 0 && kNAs == kNWs,
-                      "uniform copies, equal scale halves");
+                          kSegWs % NWAVES == 0,
+                      "uniform copies");
         if constexpr (I < kNA) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(sa + (wave + I * NWAVES) * 1024), 16, oa[I],
                                                      kb * 32, 0, 0);
@@ -196,10 +200,11 @@ struct BufStage {
         } else if constexpr (I < kAll) {
             constexpr int J = I - kNA - kNW;
             const int seg = wave + J * NWAVES;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wside ? rws : ras,
-                                                     (lds_void *)((wside ? sws : sas) + seg * 64), 4,
-                                                     wside ? ows[J] : oas[J],
-                                                     wside ? kbs * 4 : (kbs >> a_shift) * 4, 0, 0);
+            if (wside ? J < kNWs : J < kNAs)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wside ? rws : ras,
+                                                         (lds_void *)((wside ? sws : sas) + seg * 64), 4,
+                                                         wside ? ows[J < kNWs ? J : 0] : oas[J < kNAs ? J : 0],
+                                                         wside ? kbs * 4 : (kbs >> a_shift) * 4, 0, 0);
         }
     }
 
@@ -218,11 +223,13 @@ struct BufStage {
                                                          kb * 32, 0, 0);
         }
 #pragma unroll
-        for (int j = 0; j < kNAs; ++j) {
+        for (int j = 0; j < kNSc; ++j) {
             const int seg = wave + j * NWAVES;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wside ? rws : ras, (lds_void *)((wside ? sws : sas) + seg * 64),
-                                                     4, wside ? ows[j] : oas[j],
-                                                     wside ? kbs * 4 : (kbs >> a_shift) * 4, 0, 0);
+            if (wside ? j < kNWs : j < kNAs)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wside ? rws : ras,
+                                                         (lds_void *)((wside ? sws : sas) + seg * 64), 4,
+                                                         wside ? ows[j < kNWs ? j : 0] : oas[j < kNAs ? j : 0],
+                                                         wside ? kbs * 4 : (kbs >> a_shift) * 4, 0, 0);
         }
     }
 
@@ -358,12 +365,12 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
     using G = Geo<BM, BN, WM, WN>;
     constexpr int TM = G::kTM, TN = G::kTN;
     using St = Stage<BM, BN>;
-    // kSc8 -- the 128 x 128 shape with a ring of 2 and the 64 x 64 shape with
-    // a ring of 4 (K split or not): operands in RING OpStage buffers, scales in
+    // kSc8 -- the 256 x 128 and 128 x 128 shapes with a ring of 2 and the 64 x 64
+    // shape with a ring of 4 (K split or not): operands in RING OpStage buffers, scales in
     // Sc8Stage buffers of 8 blocks (2 for a ring of 2; 3 for a ring of 4,
     // whose copies run three stages ahead), and each stage's copies spread
     // over the units that compute the stage before them.
-    constexpr bool kSc8 = (RING == 2 && KG == 1 && !SPLIT && BM == 128 && BN == 128) ||
+    constexpr bool kSc8 = (RING == 2 && KG == 1 && !SPLIT && (BM == 128 || BM == kGemmTallBM) && BN == 128) ||
                           (RING == 4 && KG == 1 && BM == 64 && BN == 64);
     constexpr int kScBufs = RING == 2 ? 2 : 3;
     // units that carry the copies: a ring of 2 leaves the copies one stage to
@@ -394,7 +401,7 @@ __global__ __launch_bounds__(BM * BN / (WM * WN) * 64 * KG, WG_PER_CU) void gemm
         slice = blockIdx.x / (tiles_m * tiles_n);
         tile = blockIdx.x % (tiles_m * tiles_n);
     }
-    tile_of(tile, tiles_m, tiles_n, tm, tn);
+    tile_of<BM == kGemmTallBM ? kGemmTallGroupM : kGemmGroupM>(tile, tiles_m, tiles_n, tm, tn);
     const uint32_t m0 = tm * BM, n0 = tn * BN;
     const uint32_t nb = K / 32;
     const uint32_t all_stages = (nb + kGemmStageBlocks - 1) / kGemmStageBlocks;
@@ -685,6 +692,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
         const int8_t *__restrict__, const int8_t *__restrict__, const float *__restrict__,                  \
         const float *__restrict__, uint16_t *__restrict__, uint32_t, uint32_t, uint32_t, uint32_t, uint32_t, \
         uint32_t, uint32_t, float *__restrict__, uint64_t, uint32_t);
+BSR_GEMM_INST(256, 128, 64, 64, 1, 1, 2, false)
 BSR_GEMM_INST(128, 128, 64, 64, 2, 1, 2, false)
 BSR_GEMM_INST(32, 32, 32, 32, 1, 8, 2, false)
 BSR_GEMM_INST(32, 32, 32, 32, 2, 4, 2, false)
@@ -717,19 +725,21 @@ hipError_t launch_tiles(const int8_t *a_i8, const int8_t *w_i8, const float *a_s
 hipError_t launch_gemm(const int8_t *a_i8, const int8_t *w_i8, const float *a_scale, uint32_t a_ld,
                        uint32_t a_shift, const float *w_scale, uint16_t *out, uint32_t m, uint32_t n,
                        uint32_t k, bool split_k, hipStream_t s) {
-    // Grids of at least two 128x128 tiles per CU: two 4-wave 128x128
-    // workgroups per CU (LDS 2 x 80 KB, 2 x 4 waves of 216 VGPRs); their
-    // barriers fall at different times, so one computes while the other waits
-    // (measured faster than one 8-wave 256x128 workgroup per CU at
-    // 2048x4096x4096 and 4096x28672x4096).  Smaller grids -- every m <= 128,
+    // Grids of at least two 128x128 tiles per CU: one 8-wave 256x128
+    // workgroup per CU (LDS 120 KB, 8 waves of about 214 VGPRs) where its
+    // 256-row tiling pads M no more than 128-row tiles and K < 2^24, else two
+    // 4-wave 128x128 workgroups per CU (LDS 2 x 80 KB, 216 VGPRs), whose
+    // barriers fall at different times.  Smaller grids -- every m <= 128,
     // and e.g. m = 512 at n = 4096 -- take 64x64 tiles of four 32x32 waves:
     // four times the workgroups, 1.1-2.5x faster from m = 17 to 1024 on the
     // decode and attention widths; their 4-deep ring (three stages in flight)
     // and 8-block scale stages fit 76 KB of LDS, two workgroups per CU.  Per
     // output the blocks are accumulated in the same order in both, so the bits
     // do not depend on the shape chosen.
-    const uint64_t big_tiles = div_up(m, kGemmBM) * div_up(n, kGemmBN);
-    if (m > (uint32_t)kGemmBM && big_tiles >= 2 * (uint64_t)kGemmCus)
+    if (gemm_tall_tiles(m, n, k))
+        return launch_tiles<kGemmTallBM, kGemmBN, 64, 64, 1>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, a_ld,
+                                                             a_shift, s);
+    if (gemm_big_tiles(m, n))
         return launch_tiles<kGemmBM, kGemmBN, 64, 64, 2>(a_i8, w_i8, a_scale, w_scale, out, m, n, k, a_ld,
                                                          a_shift, s);
     // Small grids, when K may be split inside a workgroup (its K groups each

@@ -130,7 +130,8 @@ def _copy_scale(directory, counter):
 
 def default_named():
     """The launches bench.py's counters are summarized for, by workload: the
-    prefill GEMM (128 x 128 tiles of 256 lanes), the weight requant (one
+    prefill GEMM (256 x 128 tiles of 512 lanes: every prefill workload's M is a
+    multiple of 256), the weight requant (one
     32-element block per lane, 256 lanes per workgroup) and the activation
     requant (four lanes per block, two 8-element chunks per lane), with their
     algorithmic bytes per launch."""
@@ -141,9 +142,9 @@ def default_named():
         for p in inputs.workload(wl).projections:
             m, n, k = p.m, p.n, p.k
             tag = p.name
-            gemm_grid = math.ceil(m / 128) * math.ceil(n / 128) * 256
+            gemm_grid = math.ceil(m / 256) * math.ceil(n / 128) * 512
             named[f"gemm_kernel|{tag}"] = dict(
-                kernel="gemm_kernel<128, 128, 64, 64, 2, 1, 2, false>", grid=gemm_grid,
+                kernel="gemm_kernel<256, 128, 64, 64, 1, 1, 2, false>", grid=gemm_grid,
                 workload=f"GEMM {m}x{n}x{k} ({tag})",
                 alg=m * k + n * k + (m + n) * (k // 32) * 4 + 2 * m * n)
             named[f"requant_w_kernel|{tag}"] = dict(

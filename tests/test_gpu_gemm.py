@@ -55,13 +55,16 @@ def test_gemm_parity_random(m, n, k):
     _check(f"gemm {m}x{n}x{k}", host(out), y, t, k)
 
 
-def test_gemm_big_tiles_ragged():
-    # m > 128 with at least 512 tiles of 128 x 128 takes the big-tile kernel; here the
-    # last tile row (1024..1099), the last tile column (7296..7399) and the last K stage
-    # (33 blocks: 8 stages of 4 and one of 1) are all partial.  Rows are independent,
-    # so sampled rows (both sides of each tile edge) are checked whole against the
-    # oracle, and guard bands around the output catch stores past its end.
-    m, n, k = 1100, 7400, 1056
+# m > 128 with at least 512 tiles of 128 x 128 takes the big tiles: 256 x 128 at
+# m = 1200 (m % 256 = 176, last tile row 1024..1199), 128 x 128 at m = 1100 (a
+# 256-row tiling would pad it; last tile row 1024..1099).  The last tile column
+# (7296..7399) and the last K stage (33 blocks: 8 stages of 4 and one of 1) are
+# partial too.  Rows are independent, so sampled rows (both sides of each tile
+# edge) are checked whole against the oracle, and guard bands around the output
+# catch stores past its end.
+@pytest.mark.parametrize("m", [1100, 1200])
+def test_gemm_big_tiles_ragged(m):
+    n, k = 7400, 1056
     assert m > 128 and -(-m // 128) * -(-n // 128) >= 512
     a, w, a_s, w_s = _rand_operands(4242, m, n, k, zero_frac=0.02)
     pad = 4096
@@ -72,7 +75,7 @@ def test_gemm_big_tiles_ragged():
     assert np.all(hb[:pad] == 0x7B7B) and np.all(hb[pad + m * n:] == 0x7B7B)
     # ... and every element inside was written (0x7B7B, ~2^119, is far above any result here)
     assert not np.any(hb[pad:pad + m * n] == 0x7B7B)
-    rows = np.array([0, 1, 127, 128, 555, 1023, 1024, 1050, 1098, 1099])
+    rows = np.array([0, 1, 127, 128, 255, 256, 555, 1023, 1024, 1050, m - 2, m - 1])
     y, t = oracle.gemm_ref(a[rows], w, a_s[rows], w_s)
     _check(f"gemm big tiles {m}x{n}x{k}, rows {rows.tolist()}",
            hb[pad:pad + m * n].reshape(m, n)[rows], y, t, k)
@@ -445,7 +448,9 @@ def _padded(arr, fill, pad_bytes=512):
 # the end of its second scale stage (1 block: one stage; 7 blocks: two stages
 # in one scale stage); the small-grid and GEMV shapes run too.
 @pytest.mark.parametrize("m,n,k,path", [(1100, 7400, 416, bsr.PATH_GEMM), (1100, 7400, 32, bsr.PATH_GEMM),
-                                        (1100, 7400, 224, bsr.PATH_GEMM), (300, 260, 160, bsr.PATH_GEMM),
+                                        (1100, 7400, 224, bsr.PATH_GEMM), (1200, 7400, 416, bsr.PATH_GEMM),
+                                        (1200, 7400, 32, bsr.PATH_GEMM), (1200, 7400, 224, bsr.PATH_GEMM),
+                                        (300, 260, 160, bsr.PATH_GEMM),
                                         (40, 70, 160, bsr.PATH_AUTO), (8, 70, 416, bsr.PATH_AUTO),
                                         (8, 70, 160, bsr.PATH_INVARIANT), (20, 300, 224, bsr.PATH_INVARIANT)])
 def test_tail_reads_ignore_bytes_past_buffers(m, n, k, path):
@@ -458,14 +463,16 @@ def test_tail_reads_ignore_bytes_past_buffers(m, n, k, path):
     _check(f"poisoned tails {m}x{n}x{k}", host(out), y, t, k)
 
 
-def test_tail_reads_ignore_bytes_past_buffers_agroup():
+@pytest.mark.parametrize("m", [1100, 1200])
+def test_tail_reads_ignore_bytes_past_buffers_agroup(m):
     """The same with activation scales per 128 elements and per row on the big
-    tiles: K = 1152 is 36 blocks, 9 stages, so the last 8-block scale stage
-    holds 4 blocks past the end (one 128-element group past each row)."""
-    m, n, k = 1100, 7400, 1152
+    tiles (128 x 128 at m = 1100, 256 x 128 at m = 1200): K = 1152 is 36
+    blocks, 9 stages, so the last 8-block scale stage holds 4 blocks past the
+    end (one 128-element group past each row)."""
+    n, k = 7400, 1152
     a, w, _, w_s = _rand_operands(77, m, n, k)
     rng = np.random.default_rng(78)
-    rows = np.array([0, 127, 128, 1023, 1024, 1099])
+    rows = np.array([0, 127, 128, 255, 256, 1023, 1024, m - 1])
     for group in (128, 0):
         ng = 1 if group == 0 else k // group
         a_s = (rng.uniform(0.5, 2.0, size=(m, ng)) * 2.0 ** -8).astype(np.float32)

@@ -151,15 +151,19 @@ def test_invariant_path_errors():
 
 @pytest.mark.parametrize("k", [512, 544])
 def test_rows_equal_across_gemm_tile_shapes(k):
-    """A 2048-row GEMM at N = 4096 runs 128x128 tiles; 100 of its rows alone run
-    64x64 tiles, and 16 of them the chain GEMV: the same bits every time.  The
-    128x128 tiles stage scales 8 blocks at a time: K = 544 (17 blocks, 5
-    stages) ends in a scale stage with one live block."""
+    """A 2048-row GEMM at N = 4096 runs 256x128 tiles; the same rows inside a
+    2112-row GEMM run 128x128 tiles (a 256-row tiling would pad 2112); 100 of
+    them alone run 64x64 tiles, and 16 of them the chain GEMV: the same bits
+    every time.  The big tiles stage scales 8 blocks at a time: K = 544 (17
+    blocks, 5 stages) ends in a scale stage with one live block."""
     m, n = 2048, 4096
     a, packed, e4m3 = _operands(11, m, n, k)
     w_i8, w_s = gpu_requant_w(packed, e4m3, inputs.SCALE2_1_448)
     a_i8, a_s = gpu_requant_a(a)
     full = host(gpu_gemm(a_i8, w_i8, a_s, w_s, path=bsr.PATH_INVARIANT))
+    wider = host(gpu_gemm(torch.cat([a_i8, a_i8[:64]]).contiguous(), w_i8, torch.cat([a_s, a_s[:64]]).contiguous(),
+                          w_s, path=bsr.PATH_INVARIANT))
+    assert np.array_equal(wider[:m], full)
     for lo, hi in [(5, 105), (1000, 1016), (1900, 2048)]:
         part = host(gpu_gemm(a_i8[lo:hi].contiguous(), w_i8, a_s[lo:hi].contiguous(), w_s,
                              path=bsr.PATH_INVARIANT))

@@ -39,3 +39,14 @@ def test_gemm_split_plan(tmp_path):
     assert out.startswith("ok ")
     cases, split = map(int, out.split()[1:])
     assert split > 1000 and cases > split
+
+
+def test_gemm_big_tile_choice(tmp_path):
+    """The 256 x 128 tile runs only on grids of at least two 128 x 128 tiles per
+    CU, only where its tiling pads M no more than 128-row tiles, and only for
+    K whose 256 rows fit 32-bit offsets; the prefill workloads take it."""
+    rc, out = _run_checker("gemm_plan_check", tmp_path)
+    assert rc == 0, out
+    assert out.startswith("ok ")
+    cases, tall = map(int, out.split()[1:])
+    assert tall > 1000 and cases > tall
