@@ -213,3 +213,42 @@ def test_sweep_invariance(i):
         y, t = oracle.gemm_ref_agroup(sel[0], w, sel[1], w_s, group if group else k)
     res = check_bf16(got_small, y, t, k)
     assert res.ok, res
+
+
+def _big_cases(seed=20240612, count=10):
+    """Grids of at least two 128 x 128 tiles per CU (the big tiles: 256 x 128
+    where M's 256-row tiling pads no more than 128-row tiles, else 128 x 128),
+    with M residues on both sides of that choice and short K."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        m = int(rng.integers(129, 3000))
+        n = int(rng.integers(1, 9000))
+        k = 32 * int(rng.integers(1, 48))
+        if -(-m // 128) * -(-n // 128) >= 512:
+            out.append((len(out), m, n, k))
+    return out
+
+
+@pytest.mark.parametrize("i,m,n,k", _big_cases(), ids=str)
+def test_sweep_big_grids(i, m, n, k):
+    say(f"sweep big grid case {i}: m={m} n={n} k={k} (m % 256 = {m % 256})")
+    rng = np.random.default_rng(8000 + i)
+    a = rng.integers(-127, 128, size=(m, k)).astype(np.int8)
+    w = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
+    a_s = (rng.uniform(0.5, 2.0, size=(m, k // 32)) * 2.0 ** rng.integers(-12, -2, size=(m, k // 32))
+           ).astype(np.float32)
+    w_s = (rng.uniform(0.5, 2.0, size=(n, k // 32)) * 2.0 ** rng.integers(-14, -4, size=(n, k // 32))
+           ).astype(np.float32)
+    out = canary_out(m, n)
+    bsr.int8_gemm_blockscaled(to_dev(a), to_dev(w), to_dev(a_s), to_dev(w_s), out)
+    got = host(out)
+    assert not np.any(got == 0x7FA5), "every output written"
+    # every 128-row band (a random row in each), both edges of every 256-row tile, the last row
+    rows = sorted({int(r) for b in range(0, m, 128) for r in [b + rng.integers(0, min(128, m - b))]} |
+                  {r for t in range(0, m, 256) for r in (t, min(t + 255, m - 1))} | {m - 1})
+    rows = np.array(rows)
+    y, t = oracle.gemm_ref(a[rows], w, a_s[rows], w_s)
+    res = check_bf16(got[rows], y, t, k)
+    say(f"  {len(rows)} rows: {res}")
+    assert res.ok, f"big grid case {i} {m}x{n}x{k}: {res}"
