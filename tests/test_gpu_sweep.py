@@ -174,8 +174,8 @@ def test_sweep_w4a16(i, m, k):
 
 # Path invariance over seeded random shapes: under BSR_PATH_INVARIANT the rows
 # of an m <= 16 call (the chain GEMV) have the same bits as the same rows placed
-# at a random offset inside a larger call (the GEMM without its K split, 64 x 64
-# or 128 x 128 tiles as the grid decides), with grouped activation scales too.
+# at a random offset inside a larger call (the GEMM without its K split, in
+# whichever tiles the grid takes), with grouped activation scales too.
 @pytest.mark.parametrize("i", range(24), ids=str)
 def test_sweep_invariance(i):
     rng = np.random.default_rng(7000 + i)
