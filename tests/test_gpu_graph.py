@@ -118,3 +118,47 @@ def test_split_k_and_noalloc_replay_in_graph():
         assert torch.equal(got[0], out_ws) and torch.equal(got[1], out_na), f"replay {rep}"
         assert torch.equal(out_ws, out_na)
         say(f"graph replay {rep}: split-K GEMM (workspace and static scratch) equals the eager launches")
+
+
+def test_big_grid_prefill_replays_in_graph():
+    """A prefill on a grid of two 128 x 128 tiles per CU (the 256 x 128 tile) and
+    one whose M a 256-row tiling would pad (the 128 x 128 tile), captured in one
+    graph: three replays on new activations, each equal to eager launches."""
+    rng = np.random.default_rng(93)
+    n, k = 4096, 1024
+    packed, e4m3 = inputs.nvfp4_weight(rng, n, k, -4, 2)
+    w_i8, w_s = gpu_requant_w(packed, e4m3, inputs.SCALE2_1_448)
+    bufs = []
+    for m in (2048, 2112):
+        bufs.append(dict(a=_bf16(rng, m, k), a_i8=torch.empty((m, k), dtype=torch.int8, device=DEV),
+                         a_s=torch.empty((m, k // 32), dtype=torch.float32, device=DEV),
+                         out=torch.empty((m, n), dtype=torch.int16, device=DEV)))
+
+    def step():
+        for b in bufs:
+            bsr.prefill(b["a"], w_i8, w_s, b["a_i8"], b["a_s"], b["out"])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        for b in bufs:
+            b["a"].copy_(_bf16(rng, b["a"].shape[0], k))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [b["out"].clone() for b in bufs]
+        for b in bufs:
+            b["out"].zero_()
+        step()
+        torch.cuda.synchronize()
+        for g, b in zip(got, bufs):
+            assert torch.equal(g, b["out"]), f"replay {rep}, m = {b['out'].shape[0]}"
+        say(f"graph replay {rep}: big-grid prefills equal the eager launches")
